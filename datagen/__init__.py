@@ -1,0 +1,183 @@
+"""Seeded synthetic inputs for exact top-k indexer selection and selection replay.
+
+This module draws random numbers and encodes them into the storage formats the
+selection path reads (bf16 bit patterns, OCP FP8 E4M3 bytes with per-token fp32
+scales, fp32 head weights).  It holds none of the method's arithmetic: no
+scoring, no thresholds, no selection.  Both the CPU oracle (``oracle/``) and the
+HIP path (``exact_top_token_amd``) consume exactly the arrays produced here, so
+the two sides read identical bytes.
+
+Workloads (HyScale pages: the GLM-5.1 worked example on the learnaivisually
+explainer gives L = 1,048,576 keys, n = 8,192 queries per GPU, k = 2,048; the
+smaller shapes keep the same causal structure):
+
+==========  =========  =====  ==  ===  =====  =====================================
+name        L          n      H   d    k      values
+==========  =========  =====  ==  ===  =====  =====================================
+tiny        4,096      256    4   64   256    q,k ints U{-3..3} (bf16), w ints U{1,2}
+mid         131,072    2,048  64  128  2,048  q,k ~ N(0,1)/sqrt(d) bf16, w ~ U(0,1)/H
+glm1m       1,048,576  8,192  64  128  2,048  as mid
+glm1m_fp8   1,048,576  8,192  64  128  2,048  glm1m's fp32 draws, per-token E4M3
+stress_a    1,048,576  8,192  64  128  2,048  clustered keys + planted failures
+stress_b    1,048,576  8,192  64  128  2,048  clustered keys + >64 planted failures
+==========  =========  =====  ==  ===  =====  =====================================
+
+The queries always sit at the last n positions: query i has position
+``q_start + i`` with ``q_start = L - n`` and sees keys ``0 .. q_start + i``.
+
+Draw order for every config: q, then k, then w, from
+``numpy.random.default_rng(seed)``; fp32 draws are rounded to bf16 with
+round-to-nearest-even.
+"""
+from __future__ import annotations
+
+import dataclasses
+import math
+
+import numpy as np
+
+__all__ = [
+    "CONFIGS", "Inputs", "make", "make_custom", "f32_to_bf16_bits",
+    "f32_to_e4m3", "quantize_e4m3_per_row", "subset_queries",
+]
+
+CONFIGS = {
+    "tiny": dict(L=4096, n=256, H=4, d=64, k=256, dtype="bf16", dist="int", seed=1001),
+    "mid": dict(L=131072, n=2048, H=64, d=128, k=2048, dtype="bf16", dist="normal", seed=1002),
+    "glm1m": dict(L=1048576, n=8192, H=64, d=128, k=2048, dtype="bf16", dist="normal", seed=1003),
+    "glm1m_fp8": dict(L=1048576, n=8192, H=64, d=128, k=2048, dtype="fp8", dist="normal", seed=1003),
+}
+
+
+@dataclasses.dataclass
+class Inputs:
+    """One selection problem in storage form.
+
+    ``q`` is ``[n][H][d]`` and ``k`` is ``[L][d]``: uint16 bf16 bit patterns, or
+    uint8 OCP E4M3 codes when ``dtype == "fp8"`` (then ``q_scale[n]`` and
+    ``k_scale[L]`` are the fp32 per-token dequantisation scales).  ``w`` is
+    ``[n][H]`` fp32.  Query ``i`` sits at position ``q_start + i``.
+    """
+    name: str
+    L: int
+    n: int
+    H: int
+    d: int
+    k: int
+    dtype: str
+    q: np.ndarray
+    k_: np.ndarray
+    w: np.ndarray
+    q_scale: np.ndarray | None = None
+    k_scale: np.ndarray | None = None
+
+    @property
+    def q_start(self) -> int:
+        return self.L - self.n
+
+
+def f32_to_bf16_bits(x: np.ndarray) -> np.ndarray:
+    """Round fp32 values to bf16 (round to nearest, ties to even); return the
+    16-bit patterns.  Inputs are finite."""
+    u = np.ascontiguousarray(x, dtype=np.float32).view(np.uint32).astype(np.uint64)
+    lsb = (u >> np.uint64(16)) & np.uint64(1)
+    r = (u + np.uint64(0x7FFF) + lsb) >> np.uint64(16)
+    return r.astype(np.uint16)
+
+
+def _e4m3_magnitudes() -> np.ndarray:
+    """Magnitudes of the non-negative finite OCP E4M3 codes 0x00..0x7E, in code
+    order (which is also ascending order).  Exponent bias 7; exponent field 0
+    is subnormal (m/8 * 2^-6); code 0x7F is NaN and is never produced."""
+    mags = np.empty(127, dtype=np.float64)
+    for c in range(127):
+        e, m = c >> 3, c & 7
+        mags[c] = (m / 8.0) * 2.0 ** -6 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    return mags
+
+
+_E4M3_MAGS = _e4m3_magnitudes()
+
+
+def f32_to_e4m3(x: np.ndarray) -> np.ndarray:
+    """Encode values to OCP E4M3 codes: round to nearest, ties to even code,
+    saturating to +-448."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 448.0)
+    hi = np.searchsorted(_E4M3_MAGS, a, side="left")      # first mag >= a
+    hi = np.minimum(hi, 126)
+    lo = np.maximum(hi - 1, 0)
+    d_hi = _E4M3_MAGS[hi] - a
+    d_lo = a - _E4M3_MAGS[lo]
+    pick_lo = (d_lo < d_hi) | ((d_lo == d_hi) & ((lo & 1) == 0))
+    code = np.where(pick_lo, lo, hi).astype(np.uint8)
+    sign = np.signbit(x).astype(np.uint8) << 7
+    return (code | sign).astype(np.uint8)
+
+
+def quantize_e4m3_per_row(x32: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
+    """Per-token quantisation: the leading axis is the token.  scale = amax/448
+    in fp32 (1 for an all-zero token); codes = E4M3(x / scale)."""
+    rows = x32.reshape(x32.shape[0], -1).astype(np.float32)
+    amax = np.abs(rows).max(axis=1)
+    scale = np.where(amax > 0, amax / np.float32(448.0), np.float32(1.0)).astype(np.float32)
+    codes = np.empty(rows.shape, dtype=np.uint8)
+    step = max(1, (1 << 22) // max(1, rows.shape[1]))
+    for a in range(0, rows.shape[0], step):
+        b = min(rows.shape[0], a + step)
+        codes[a:b] = f32_to_e4m3(rows[a:b].astype(np.float64) / scale[a:b, None].astype(np.float64))
+    return codes.reshape(x32.shape), scale
+
+
+def _draw(cfg: dict, rng: np.random.Generator):
+    L, n, H, d = cfg["L"], cfg["n"], cfg["H"], cfg["d"]
+    if cfg["dist"] == "int":
+        q = rng.integers(-3, 4, size=(n, H, d)).astype(np.float32)
+        k = rng.integers(-3, 4, size=(L, d)).astype(np.float32)
+        w = rng.integers(1, 3, size=(n, H)).astype(np.float32)
+    elif cfg["dist"] == "normal":
+        s = np.float32(1.0 / math.sqrt(d))
+        q = rng.standard_normal((n, H, d), dtype=np.float32) * s
+        k = rng.standard_normal((L, d), dtype=np.float32) * s
+        w = rng.random((n, H), dtype=np.float32) / np.float32(H)
+    else:
+        raise ValueError(cfg["dist"])
+    return q, k, w
+
+
+def make_custom(name: str, L: int, n: int, H: int, d: int, k: int, dtype: str = "bf16",
+                dist: str = "normal", seed: int = 0) -> Inputs:
+    """Draw a problem of any shape with one of the two value recipes."""
+    cfg = dict(L=L, n=n, H=H, d=d, k=k, dtype=dtype, dist=dist, seed=seed)
+    if not (0 < n <= L):
+        raise ValueError("need 0 < n <= L")
+    rng = np.random.default_rng(seed)
+    q32, k32, w = _draw(cfg, rng)
+    if dtype == "bf16":
+        return Inputs(name, L, n, H, d, k, dtype, f32_to_bf16_bits(q32), f32_to_bf16_bits(k32), w)
+    if dtype == "fp8":
+        qc, qs = quantize_e4m3_per_row(q32)
+        kc, ks = quantize_e4m3_per_row(k32)
+        return Inputs(name, L, n, H, d, k, dtype, qc, kc, w, qs, ks)
+    raise ValueError(dtype)
+
+
+def make(name: str) -> Inputs:
+    """The named workload (see the module table)."""
+    if name.startswith("stress"):
+        from . import stress
+        return stress.make(name)
+    cfg = CONFIGS[name]
+    return make_custom(name, cfg["L"], cfg["n"], cfg["H"], cfg["d"], cfg["k"],
+                       cfg["dtype"], cfg["dist"], cfg["seed"])
+
+
+def subset_queries(n: int, count: int = 64, seed: int = 7, must: tuple[int, ...] = ()) -> np.ndarray:
+    """A seeded sorted subset of query indices that always holds the first and
+    last query and every index in ``must``."""
+    base = {0, n - 1, *[int(m) for m in must if 0 <= m < n]}
+    rng = np.random.default_rng(seed)
+    pool = np.setdiff1d(np.arange(n), np.fromiter(base, dtype=np.int64))
+    extra = max(0, min(count - len(base), pool.size))
+    pick = rng.choice(pool, size=extra, replace=False) if extra else np.empty(0, np.int64)
+    return np.sort(np.concatenate([np.fromiter(base, dtype=np.int64), pick.astype(np.int64)]))

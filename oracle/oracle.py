@@ -1,0 +1,285 @@
+"""CPU fp64 oracle for exact top-k indexer selection and selection replay.
+
+TEST INFRASTRUCTURE ONLY.  Nothing on the product path may import, call or link
+this module: only ``tests/``, ``__graft_entry__.smoke()`` and the CPU-baseline
+leg of ``bench.py`` use it.  It shares no code, tables or helpers with the HIP
+path; both sides read the same input bytes from ``datagen``.
+
+Sources, cited by page title and passage:
+
+* [Explainer] "HyScale sparse-attention training -- Selection without a score
+  table -- What does it mean?" (learnaivisually.com).  Paragraphs: *contest*
+  (the score table and the two-kernel baseline), *key observation* (selection
+  outputs indices; top-k is not differentiable), *HyTopK* (sampled threshold,
+  candidate buffer, check, recovery, fallback above 64 failures, radix select
+  over positions, radix sort), *selection replay*, *worked example* (the
+  GLM-5.1 figures at L = 1,048,576).
+* [Summary] "HyScale: Scaling Long-Context Training for Learned Sparse
+  Attention" (neuraltrendhub.com), section *What the paper found*.
+* [Abstract] the paper's abstract (reproduced on zhuanzhiai.com and in the
+  Summary's *Original abstract* section).
+
+What this oracle computes is the plain definition, because the method reaches
+exactly that result [Abstract: HyTopK finds each query's exact top-k without a
+score table]:
+
+1. decode the stored inputs exactly to fp64 (bf16 bits; OCP E4M3 codes times
+   their per-token fp32 scales; fp32 head weights);
+2. score every causal pair (query position t sees keys 0..t) with the
+   learned-sparse-attention indexer I(t,s) = sum_h w[t,h] * ReLU(q[t,h] . k[s]).
+   The pages do not print the indexer's formula; they say its scores are the
+   same kind of work as attention scores [Explainer, contest] and that the
+   architecture descends from DeepSeek-V3.2 [Abstract].  This is the standard
+   form of that indexer: the head weight applies after the ReLU;
+3. order the context by score descending, then position ascending (lower
+   position wins a tie) and keep the first min(k, ctx); pad with -1 / -inf;
+4. replay: I(t, idx) at the saved indices [Explainer, selection replay].
+
+The threshold model (``sample_count`` .. ``predict_paths``) is not part of the
+result.  It restates the HyTopK paragraph and the worked example so tests can
+pin the GPU's statistics, failure sets and path choice.
+"""
+from __future__ import annotations
+
+import math
+
+import numpy as np
+
+NEG_INF = float("-inf")
+
+# ---------------------------------------------------------------------------
+# 1. Exact decoding of the storage formats.
+# ---------------------------------------------------------------------------
+
+
+def decode_bf16(bits: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> fp64, from the format: 1 sign bit, 8 exponent bits
+    (bias 127), 7 fraction bits; exponent 0 is subnormal (f/128 * 2^-126),
+    exponent 255 is inf/NaN."""
+    b = np.asarray(bits, dtype=np.uint16).astype(np.int64)
+    sign = np.where((b >> 15) & 1, -1.0, 1.0)
+    e = (b >> 7) & 0xFF
+    f = (b & 0x7F).astype(np.float64)
+    normal = sign * (1.0 + f / 128.0) * np.exp2(e.astype(np.float64) - 127.0)
+    sub = sign * (f / 128.0) * 2.0 ** -126
+    out = np.where(e == 0, sub, normal)
+    special = e == 0xFF
+    if np.any(special):
+        out = np.where(special & (f == 0), sign * np.inf, out)
+        out = np.where(special & (f != 0), np.nan, out)
+    return out
+
+
+def decode_e4m3(codes: np.ndarray) -> np.ndarray:
+    """OCP FP8 E4M3 codes -> fp64, from the format: 1 sign bit, 4 exponent bits
+    (bias 7), 3 mantissa bits; exponent 0 is subnormal (m/8 * 2^-6); the codes
+    with all exponent and mantissa bits set (0x7F, 0xFF) are NaN; there is no
+    infinity, so the largest finite value is 1.75 * 2^8 = 448."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64)
+    sign = np.where((c >> 7) & 1, -1.0, 1.0)
+    e = (c >> 3) & 0xF
+    m = (c & 0x7).astype(np.float64)
+    normal = sign * (1.0 + m / 8.0) * np.exp2(e.astype(np.float64) - 7.0)
+    sub = sign * (m / 8.0) * 2.0 ** -6
+    out = np.where(e == 0, sub, normal)
+    return np.where((c & 0x7F) == 0x7F, np.nan, out)
+
+
+class Decoded:
+    """Exact fp64 view of one problem.  Queries are decoded on demand (the
+    1M-key shapes hold 8,192 x 64 x 128 query values)."""
+
+    def __init__(self, inp):
+        self.inp = inp
+        self.L, self.n, self.H, self.d, self.k = inp.L, inp.n, inp.H, inp.d, inp.k
+        self.q_start = inp.L - inp.n
+        if inp.dtype == "bf16":
+            self.keys = decode_bf16(inp.k_)
+        elif inp.dtype == "fp8":
+            self.keys = decode_e4m3(inp.k_) * inp.k_scale.astype(np.float64)[:, None]
+        else:
+            raise ValueError(inp.dtype)
+
+    def query(self, i: int) -> tuple[np.ndarray, np.ndarray]:
+        """(q[i] as [H][d] fp64, w[i] as [H] fp64)."""
+        inp = self.inp
+        if inp.dtype == "bf16":
+            q = decode_bf16(inp.q[i])
+        else:
+            q = decode_e4m3(inp.q[i]) * float(inp.q_scale[i])
+        return q, inp.w[i].astype(np.float64)
+
+    def position(self, i: int) -> int:
+        return self.q_start + int(i)
+
+
+# ---------------------------------------------------------------------------
+# 2. Indexer scores.
+# ---------------------------------------------------------------------------
+
+
+def score_row(dec: Decoded, i: int, chunk: int = 32768) -> np.ndarray:
+    """I(t, s) for query i (position t) and every key s = 0..t, in fp64."""
+    q, w = dec.query(i)
+    ctx = dec.position(i) + 1
+    out = np.empty(ctx, dtype=np.float64)
+    for a in range(0, ctx, chunk):
+        b = min(ctx, a + chunk)
+        dots = q @ dec.keys[a:b].T            # [H][b-a]  q[t,h] . k[s]
+        np.maximum(dots, 0.0, out=dots)       # ReLU
+        out[a:b] = w @ dots                   # sum_h w[t,h] * ...
+    return out
+
+
+def score_pairs(dec: Decoded, i: int, keys: np.ndarray) -> np.ndarray:
+    """I(t, s) for query i at the given key positions (any order)."""
+    q, w = dec.query(i)
+    dots = q @ dec.keys[np.asarray(keys, dtype=np.int64)].T
+    return w @ np.maximum(dots, 0.0)
+
+
+# ---------------------------------------------------------------------------
+# 3. Exact top-k under the tie rule, and replay.
+# ---------------------------------------------------------------------------
+
+
+def exact_topk(row: np.ndarray, k: int) -> tuple[np.ndarray, np.ndarray]:
+    """Keep the min(k, ctx) best keys of one score row: score descending, then
+    position ascending.  Returns (idx int64 [k], score fp64 [k]) padded with
+    -1 / -inf."""
+    ctx = row.shape[0]
+    order = np.lexsort((np.arange(ctx), -row))   # last key is the primary key
+    keep = order[: min(k, ctx)]
+    idx = np.full(k, -1, dtype=np.int64)
+    val = np.full(k, NEG_INF, dtype=np.float64)
+    idx[: keep.size] = keep
+    val[: keep.size] = row[keep]
+    return idx, val
+
+
+def select(inp, queries=None) -> tuple[np.ndarray, np.ndarray]:
+    """Exact top-k for the given query indices (default: all n).
+    Returns (idx [m][k] int64, score [m][k] fp64)."""
+    dec = Decoded(inp)
+    qs = np.arange(inp.n) if queries is None else np.asarray(queries, dtype=np.int64)
+    idx = np.empty((qs.size, inp.k), dtype=np.int64)
+    val = np.empty((qs.size, inp.k), dtype=np.float64)
+    for r, i in enumerate(qs):
+        idx[r], val[r] = exact_topk(score_row(dec, int(i)), inp.k)
+    return idx, val
+
+
+def replay(inp, idx: np.ndarray, queries=None) -> np.ndarray:
+    """Selection replay: rescore only the saved indices.  idx < 0 is padding
+    and scores -inf.  Returns fp64 [m][k]."""
+    dec = Decoded(inp)
+    qs = np.arange(inp.n) if queries is None else np.asarray(queries, dtype=np.int64)
+    idx = np.asarray(idx)
+    out = np.full(idx.shape, NEG_INF, dtype=np.float64)
+    for r, i in enumerate(qs):
+        ok = idx[r] >= 0
+        if np.any(ok):
+            out[r, ok] = score_pairs(dec, int(i), idx[r, ok])
+    return out
+
+
+# ---------------------------------------------------------------------------
+# 4. The sampled-threshold model (statistics and path prediction only).
+# ---------------------------------------------------------------------------
+
+DEFAULTS = dict(m_min=4096, m_max=8192, m_div=128, oversample=3, max_recover=64)
+
+
+def sample_count(L: int, m_min: int = 4096, m_max: int = 8192, m_div: int = 128) -> int:
+    """M = min(max(4096, L/128), 8192) [Explainer, worked example], with L the
+    number of keys in the call and integer division."""
+    return min(max(m_min, L // m_div), m_max)
+
+
+def sample_positions(ctx: int, M: int) -> np.ndarray:
+    """Evenly spaced samples from the query's own context [Explainer, HyTopK]:
+    M_q = min(M, ctx) positions floor(j * ctx / M_q), j = 0..M_q-1."""
+    mq = min(M, ctx)
+    j = np.arange(mq, dtype=np.int64)
+    return (j * ctx) // mq
+
+
+def threshold_rank(ctx: int, k: int, mq: int, oversample: int = 3) -> int:
+    """The threshold is the ceil(3k * M / ctx)-th best sample [Explainer, worked
+    example: 48 at ctx = 1,048,576, k = 2,048, M = 8,192], clamped to [1, M_q]."""
+    r = -(-(oversample * k * mq) // ctx)
+    return max(1, min(mq, r))
+
+
+def threshold(row: np.ndarray, k: int, L: int, params: dict | None = None) -> tuple[float, int, int]:
+    """tau = the r-th largest sample score (duplicates count separately).
+    Returns (tau, r, M_q)."""
+    p = dict(DEFAULTS, **(params or {}))
+    ctx = row.shape[0]
+    M = sample_count(L, p["m_min"], p["m_max"], p["m_div"])
+    pos = sample_positions(ctx, M)
+    r = threshold_rank(ctx, k, pos.size, p["oversample"])
+    s = np.sort(row[pos])[::-1]
+    return float(s[r - 1]), r, pos.size
+
+
+def candidates(row: np.ndarray, tau: float) -> np.ndarray:
+    """Keys that pass the on-chip compare (score >= tau), in position order."""
+    return np.nonzero(row >= tau)[0]
+
+
+def predict_row(row: np.ndarray, k: int, L: int, cap: int, params: dict | None = None) -> dict:
+    """Threshold, candidate count and check verdict for one query, with the
+    margins that make a prediction robust to fp32-vs-fp64 rounding."""
+    tau, r, mq = threshold(row, k, L, params)
+    ctx = row.shape[0]
+    cnt = int(np.count_nonzero(row >= tau))
+    need = min(k, ctx)
+    near = int(np.count_nonzero(np.abs(row - tau) <= 1e-6 * (abs(tau) + 1.0)))
+    return dict(tau=tau, r=r, mq=mq, cnt=cnt, overflow=cnt > cap, underk=cnt < need,
+                fail=(cnt > cap) or (cnt < need), margin_cap=cap - cnt,
+                margin_k=cnt - need, near_tau=near)
+
+
+def predict_paths(rows: list, k: int, L: int, cap: int, params: dict | None = None) -> dict:
+    """Per-query predictions for one selection call plus the call's path:
+    recovery if 1..64 queries fail, full rescore above 64 [Explainer, HyTopK]."""
+    p = dict(DEFAULTS, **(params or {}))
+    per = [predict_row(r, k, L, cap, p) for r in rows]
+    failed = [i for i, x in enumerate(per) if x["fail"]]
+    return dict(per_query=per, failed=failed, n_failed=len(failed),
+                full_rescore=len(failed) > p["max_recover"])
+
+
+def select_from_candidates(row: np.ndarray, tau: float, cap: int, k: int):
+    """The method's own route for one query, modelled on the CPU: keep only keys
+    with score >= tau; if that set overflowed ``cap`` or holds fewer than
+    min(k, ctx) keys the query is flagged (returns None); otherwise the exact
+    top-k of the candidates.  Used only to pin the soundness claim."""
+    cand = candidates(row, tau)
+    if cand.size > cap or cand.size < min(k, row.shape[0]):
+        return None
+    sub = row[cand]
+    order = np.lexsort((cand, -sub))[: min(k, cand.size)]
+    idx = np.full(k, -1, dtype=np.int64)
+    val = np.full(k, NEG_INF)
+    idx[: order.size] = cand[order]
+    val[: order.size] = sub[order]
+    return idx, val
+
+
+def expected_candidates(ctx: int, mq: int, r: int) -> float:
+    """Mean candidate count for i.i.d. continuous scores: the r passing samples
+    plus each of the ctx - M_q other keys exceeding the r-th largest of M_q
+    i.i.d. samples with probability r / (M_q + 1)."""
+    return r + (ctx - mq) * r / (mq + 1)
+
+
+def scoring_flops(L: int, n: int, H: int, d: int) -> float:
+    """2*H*d per causal pair, summed over queries at the last n positions."""
+    pairs = n * L - n * (n - 1) // 2
+    return 2.0 * H * d * pairs
+
+
+def log2_ceil(x: int) -> int:
+    return int(math.ceil(math.log2(x))) if x > 1 else 0
