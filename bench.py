@@ -1,0 +1,253 @@
+#!/usr/bin/env python3
+"""Benchmark of the exact top-k indexer selection path on one MI355X.
+
+One step = one pass of the whole hot path over one batch of synthetic input
+already resident in HBM: hytopk_select (sampled threshold, fused score +
+compare + compaction, check, recovery / full rescore when needed, candidate
+select + sort) followed by hytopk_replay of the selected indices.
+
+Default workload: the GLM-5.1-shaped one-GPU shard of the HyScale explainer's
+worked example (L = 1,048,576 keys, n = 8,192 queries at the last positions,
+H = 64, d = 128, k = 2,048, bf16 q/k ~ N(0,1)/sqrt(d), fp32 w ~ U(0,1)/H).
+
+Prints ONE JSON line.  value = algorithmic TFLOP/s of the step (2*H*d per
+causal pair for selection plus 2*H*d per replayed entry) / step time.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}   # MI355X dense MFMA
+PEAK_HBM_GBS = 8000.0
+METRIC = "HyTopK select ms + TFLOP/s (%MFMA peak) at L=1M,n=8192,k=2048; replay ms"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+KERNEL_SOURCES = ["exact_top_token_amd/csrc/score.hip", "exact_top_token_amd/csrc/tile.h",
+                  "exact_top_token_amd/csrc/common.h"]
+
+
+def kernel_hash() -> str:
+    h = hashlib.sha256()
+    for rel in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, rel), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def scoring_flops(L: int, n: int, H: int, d: int, q_start: int) -> float:
+    pairs = sum_ctx(q_start, n)
+    return 2.0 * H * d * pairs
+
+
+def sum_ctx(q_start: int, n: int) -> int:
+    return n * (q_start + 1) + n * (n - 1) // 2
+
+
+def replay_bytes(n, H, d, k, fp8) -> int:
+    bk = 1 if fp8 else 2
+    per_entry = d * bk + 4 + 4 + (4 if fp8 else 0)
+    per_query = H * (d * bk + 4) + (4 if fp8 else 0)
+    return n * k * per_entry + n * per_query
+
+
+def cpu_baseline(inp, seconds_target: float = 15.0) -> dict:
+    """The oracle as it stands, on a bounded sample of the same workload."""
+    import numpy as np
+    import oracle
+    try:
+        from threadpoolctl import threadpool_info
+        cores = max([p.get("num_threads", 1) for p in threadpool_info()] or [1])
+    except Exception:  # pragma: no cover
+        cores = os.cpu_count() or 1
+    sub = []
+    t0 = time.perf_counter()
+    i = inp.n - 1
+    flops = 0.0
+    step = max(1, inp.n // 97)
+    while time.perf_counter() - t0 < seconds_target and i >= 0 and len(sub) < 256:
+        oracle.select(inp, [i])
+        ctx = inp.L - inp.n + i + 1
+        flops += 2.0 * inp.H * inp.d * ctx
+        sub.append(i)
+        i -= step
+    dt = time.perf_counter() - t0
+    return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": int(cores), "kind": "oracle",
+            "sample": f"oracle.select (fp64 numpy/BLAS scores + exact lexsort top-k) on "
+                      f"{len(sub)} queries of the same workload, {dt:.1f} s; "
+                      f"full call extrapolated: {dt / len(sub) * inp.n:.0f} s"}
+
+
+def main() -> int:
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=5)
+    ap.add_argument("--warmup", type=int, default=2)
+    ap.add_argument("--workload", default="glm1m", help="datagen config name")
+    ap.add_argument("--no-baseline", action="store_true", help="skip the score-table baseline")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    args = ap.parse_args()
+    if args.gpus != 1:
+        print("bench.py measures one GPU: the selection path has no multi-GPU mode in this "
+              "build (see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        return 2
+
+    import numpy as np
+    import torch
+
+    import datagen
+    import exact_top_token_amd as hk
+
+    def log(msg):
+        print(f"[bench] {msg}", file=sys.stderr, flush=True)
+
+    torch.cuda.set_device(0)
+    log(f"generating {args.workload}")
+    inp = datagen.make(args.workload)
+    fp8 = inp.dtype == "fp8"
+    dev = "cuda:0"
+    if fp8:
+        q = torch.from_numpy(inp.q).to(dev).view(torch.float8_e4m3fn)
+        k = torch.from_numpy(inp.k_).to(dev).view(torch.float8_e4m3fn)
+        qs = torch.from_numpy(inp.q_scale).to(dev)
+        ks = torch.from_numpy(inp.k_scale).to(dev)
+    else:
+        q = torch.from_numpy(inp.q.view(np.int16)).to(dev).view(torch.bfloat16)
+        k = torch.from_numpy(inp.k_.view(np.int16)).to(dev).view(torch.bfloat16)
+        qs = ks = None
+    w = torch.from_numpy(inp.w).to(dev)
+    hk.load_library()
+    ws = torch.empty(hk.select_workspace_bytes(q, k, w, inp.k), dtype=torch.uint8, device=dev)
+    idx = torch.empty((inp.n, inp.k), dtype=torch.int32, device=dev)
+    sc = torch.empty((inp.n, inp.k), dtype=torch.float32, device=dev)
+    rep = torch.empty_like(sc)
+
+    def step():
+        _, _, st = hk.select(q, k, w, inp.k, q_scale=qs, k_scale=ks, workspace=ws, out=(idx, sc),
+                             with_stats=True)
+        hk.replay(q, k, w, idx, q_scale=qs, k_scale=ks, out=rep)
+        return st
+
+    log(f"warmup {args.warmup}")
+    for _ in range(args.warmup):
+        step()
+    torch.cuda.synchronize()
+
+    log(f"timing {args.steps} steps")
+    ev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True),
+           torch.cuda.Event(enable_timing=True)) for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    hk.trace_enable(True)
+    t_start = torch.cuda.Event(enable_timing=True)
+    t_end = torch.cuda.Event(enable_timing=True)
+    t_start.record()
+    stats = None
+    for i in range(args.steps):
+        ev[i][0].record()
+        _, _, stats = hk.select(q, k, w, inp.k, q_scale=qs, k_scale=ks, workspace=ws,
+                                out=(idx, sc), with_stats=True)
+        ev[i][1].record()
+        hk.replay(q, k, w, idx, q_scale=qs, k_scale=ks, out=rep)
+        ev[i][2].record()
+    t_end.record()
+    torch.cuda.synchronize()
+    phases = hk.trace_read()
+    hk.trace_enable(False)
+    total_ms = t_start.elapsed_time(t_end)
+    ms_per_step = total_ms / args.steps
+    select_ms = float(np.median([a.elapsed_time(b) for a, b, _ in ev]))
+    replay_ms = float(np.median([b.elapsed_time(c) for _, b, c in ev]))
+
+    q_start = inp.L - inp.n
+    sel_flops = scoring_flops(inp.L, inp.n, inp.H, inp.d, q_start)
+    rep_flops = 2.0 * inp.H * inp.d * inp.n * inp.k
+    peak = PEAK_TFLOPS["fp8" if fp8 else "bf16"]
+    value = (sel_flops + rep_flops) / (ms_per_step * 1e-3) / 1e12
+    sel_tflops = sel_flops / (select_ms * 1e-3) / 1e12
+    rbytes = replay_bytes(inp.n, inp.H, inp.d, inp.k, fp8)
+    replay_gbs = rbytes / (replay_ms * 1e-3) / 1e9
+
+    launches, score_total = phases.get("score_compact", (0, 0.0))
+    score_ms = score_total / max(1, launches)
+    achieved = sel_flops / (score_ms * 1e-3) / 1e12 if score_ms > 0 else None
+
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tr = json.load(open(TRAFFIC_FILE))
+            if tr.get("kernel_hash") == kernel_hash() and tr.get("workload") == args.workload:
+                traffic = tr.get("bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    baseline_ms = None
+    if not args.no_baseline:
+        log("baseline: materialise the score table, then row top-k")
+        bws = torch.empty(hk.baseline_workspace_bytes(q, k, w, inp.k), dtype=torch.uint8, device=dev)
+        bidx = torch.empty_like(idx)
+        bsc = torch.empty_like(sc)
+        hk.baseline_select(q, k, w, inp.k, q_scale=qs, k_scale=ks, workspace=bws, out=(bidx, bsc))
+        torch.cuda.synchronize()
+        a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        a.record()
+        hk.baseline_select(q, k, w, inp.k, q_scale=qs, k_scale=ks, workspace=bws, out=(bidx, bsc))
+        b.record()
+        torch.cuda.synchronize()
+        baseline_ms = a.elapsed_time(b)
+        same = bool(torch.equal(bidx, idx) and torch.equal(bsc.view(torch.int32), sc.view(torch.int32)))
+        del bws
+        if not same:
+            log("WARNING: baseline result differs from hytopk_select")
+
+    cpu = None
+    if not args.no_cpu:
+        log("cpu baseline: oracle on a bounded sample")
+        cpu = cpu_baseline(inp, args.cpu_seconds)
+
+    line = {
+        "metric": METRIC,
+        "value": round(value, 3),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "fp8_e4m3" if fp8 else "bf16",
+        "data": "synthetic (seeded datagen; no dataset or weights)",
+        "config": {"workload": f"{args.workload}: L={inp.L} n={inp.n} (positions {q_start}..{inp.L - 1}) "
+                               f"H={inp.H} d={inp.d} k={inp.k}",
+                   "L": inp.L, "n": inp.n, "H": inp.H, "d": inp.d, "k": inp.k,
+                   "parallelism": "single GPU"},
+        "select_ms": round(select_ms, 4),
+        "select_tflops": round(sel_tflops, 2),
+        "select_mfma_frac": round(sel_tflops / peak, 4),
+        "replay_ms": round(replay_ms, 4),
+        "replay_gbs": round(replay_gbs, 1),
+        "replay_hbm_frac": round(replay_gbs / PEAK_HBM_GBS, 4),
+        "baseline_ms": None if baseline_ms is None else round(baseline_ms, 3),
+        "baseline_over_select": None if baseline_ms is None else round(baseline_ms / select_ms, 3),
+        "phases_ms": {name: round(t / max(1, c), 4) for name, (c, t) in phases.items()},
+        "stats": stats,
+        "roofline": {"bound": "mfma", "kernel": "score_tile_kernel (fused score+compare+compact)",
+                     "achieved": None if achieved is None else round(achieved, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": None if achieved is None else round(achieved / peak, 4),
+                     "traffic": traffic},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

@@ -1,0 +1,236 @@
+"""Exact top-k indexer selection (HyTopK) and selection replay on MI355X.
+
+A thin ctypes binding over ``libhytopk.so`` (``include/hytopk.h``): it only
+marshals torch tensors into pointers and sizes; every step of the selection
+runs in the library's HIP kernels on the caller's current stream.  The
+library must be built (``python -m exact_top_token_amd.build``); nothing here
+falls back to a CPU or PyTorch implementation.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+__all__ = [
+    "Problem", "Params", "Stats", "load_library", "library_path", "select", "replay",
+    "baseline_select", "select_workspace_bytes", "baseline_workspace_bytes", "HytopkError",
+    "EXPORTS", "BF16", "FP8_E4M3", "PATH_AUTO", "PATH_ROWS_ALL", "trace_enable", "trace_read",
+]
+
+BF16, FP8_E4M3 = 0, 1
+PATH_AUTO, PATH_ROWS_ALL = 0, 1
+EXPORTS = (
+    "hytopk_select_workspace", "hytopk_baseline_workspace", "hytopk_select", "hytopk_replay",
+    "hytopk_baseline_select", "hytopk_status_string", "hytopk_last_error",
+    "hytopk_trace_enable", "hytopk_trace_read",
+)
+
+
+class Problem(ctypes.Structure):
+    _fields_ = [("L", ctypes.c_int64), ("n", ctypes.c_int64), ("q_start", ctypes.c_int64),
+                ("H", ctypes.c_int32), ("d", ctypes.c_int32), ("k", ctypes.c_int32),
+                ("dtype", ctypes.c_int32)]
+
+
+class Params(ctypes.Structure):
+    _fields_ = [(f, ctypes.c_int32) for f in
+                ("m_min", "m_max", "m_div", "oversample", "cap", "max_recover", "force_path",
+                 "rows_chunk")]
+
+
+class Stats(ctypes.Structure):
+    _fields_ = [("n_overflow", ctypes.c_int32), ("n_underk", ctypes.c_int32),
+                ("n_failed", ctypes.c_int32), ("full_rescore", ctypes.c_int32),
+                ("cand_total", ctypes.c_int64), ("cand_max", ctypes.c_int32),
+                ("path", ctypes.c_int32)]
+
+    def as_dict(self) -> dict:
+        return {f: getattr(self, f) for f, _ in self._fields_}
+
+
+class TraceEntry(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 32), ("launches", ctypes.c_int32),
+                ("total_ms", ctypes.c_double)]
+
+
+class HytopkError(RuntimeError):
+    def __init__(self, status: int, msg: str):
+        super().__init__(f"hytopk status {status}: {msg}")
+        self.status = status
+
+
+_LIB = None
+
+
+def library_path() -> str:
+    return os.environ.get("HYTOPK_LIBRARY",
+                          os.path.join(os.path.dirname(os.path.abspath(__file__)), "libhytopk.so"))
+
+
+def load_library():
+    """Load libhytopk.so (raises if it has not been built)."""
+    global _LIB
+    if _LIB is not None:
+        return _LIB
+    path = library_path()
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is missing: build it with `python -m exact_top_token_amd.build`")
+    lib = ctypes.CDLL(path)
+    P, vp, sz = ctypes.POINTER, ctypes.c_void_p, ctypes.c_size_t
+    lib.hytopk_select_workspace.argtypes = [P(Problem), P(Params)]
+    lib.hytopk_select_workspace.restype = sz
+    lib.hytopk_baseline_workspace.argtypes = [P(Problem)]
+    lib.hytopk_baseline_workspace.restype = sz
+    lib.hytopk_select.argtypes = [P(Problem), P(Params), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
+                                  P(Stats)]
+    lib.hytopk_select.restype = ctypes.c_int
+    lib.hytopk_replay.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp, vp, vp]
+    lib.hytopk_replay.restype = ctypes.c_int
+    lib.hytopk_baseline_select.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hytopk_baseline_select.restype = ctypes.c_int
+    lib.hytopk_status_string.argtypes = [ctypes.c_int]
+    lib.hytopk_status_string.restype = ctypes.c_char_p
+    lib.hytopk_last_error.argtypes = []
+    lib.hytopk_last_error.restype = ctypes.c_char_p
+    lib.hytopk_trace_enable.argtypes = [ctypes.c_int]
+    lib.hytopk_trace_enable.restype = ctypes.c_int
+    lib.hytopk_trace_read.argtypes = [P(TraceEntry), ctypes.c_int]
+    lib.hytopk_trace_read.restype = ctypes.c_int
+    _LIB = lib
+    return lib
+
+
+def _check(rc: int) -> None:
+    if rc != 0:
+        lib = load_library()
+        raise HytopkError(rc, lib.hytopk_last_error().decode() or lib.hytopk_status_string(rc).decode())
+
+
+def _ptr(t):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _dtype_code(q) -> int:
+    import torch
+    if q.dtype == torch.bfloat16:
+        return BF16
+    if q.dtype in (torch.float8_e4m3fn, torch.uint8):
+        return FP8_E4M3
+    raise TypeError(f"q/k must be bfloat16 or float8_e4m3fn, got {q.dtype}")
+
+
+def _problem(q, k, w, topk: int, q_start) -> Problem:
+    n, H, d = q.shape
+    L = k.shape[0]
+    if k.shape[1] != d or tuple(w.shape) != (n, H):
+        raise ValueError("shapes must be q [n][H][d], k [L][d], w [n][H]")
+    for t in (q, k, w):
+        if not t.is_cuda or not t.is_contiguous():
+            raise ValueError("tensors must be contiguous and on the GPU")
+    return Problem(L, n, L - n if q_start is None else int(q_start), H, d, int(topk), _dtype_code(q))
+
+
+def _params(params) -> Params | None:
+    if params is None:
+        return None
+    if isinstance(params, Params):
+        return params
+    p = Params()
+    for key, val in dict(params).items():
+        setattr(p, key, int(val))
+    return p
+
+
+def _stream(t):
+    import torch
+    return ctypes.c_void_p(torch.cuda.current_stream(t.device).cuda_stream)
+
+
+def trace_enable(on: bool = True) -> bool:
+    """Bracket every library launch with hipEvents (clears the totals)."""
+    return bool(load_library().hytopk_trace_enable(1 if on else 0))
+
+
+def trace_read() -> dict:
+    """{phase: (launches, total_ms)} accumulated since tracing was enabled."""
+    lib = load_library()
+    n = lib.hytopk_trace_read(None, 0)
+    if n < 0:
+        _check(n)
+    arr = (TraceEntry * max(n, 1))()
+    n = lib.hytopk_trace_read(arr, n)
+    if n < 0:
+        _check(n)
+    return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n)}
+
+
+def select_workspace_bytes(q, k, w, topk: int, q_start=None, params=None) -> int:
+    lib = load_library()
+    prob = _problem(q, k, w, topk, q_start)
+    prm = _params(params)
+    return int(lib.hytopk_select_workspace(ctypes.byref(prob), ctypes.byref(prm) if prm else None))
+
+
+def baseline_workspace_bytes(q, k, w, topk: int, q_start=None) -> int:
+    lib = load_library()
+    return int(lib.hytopk_baseline_workspace(ctypes.byref(_problem(q, k, w, topk, q_start))))
+
+
+def select(q, k, w, topk: int, *, q_scale=None, k_scale=None, q_start=None, params=None,
+           workspace=None, out=None, with_stats: bool = False):
+    """Exact top-k per query (HyTopK).  Returns (idx int32 [n][k], score fp32
+    [n][k]) and, with ``with_stats``, a dict of what the call did."""
+    import torch
+    lib = load_library()
+    prob = _problem(q, k, w, topk, q_start)
+    prm = _params(params)
+    need = int(lib.hytopk_select_workspace(ctypes.byref(prob), ctypes.byref(prm) if prm else None))
+    if need == 0:
+        _check(lib.hytopk_select(ctypes.byref(prob), ctypes.byref(prm) if prm else None,
+                                 *([None] * 8), 0, None, None))
+    if workspace is None:
+        workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    if out is None:
+        idx = torch.empty((prob.n, prob.k), dtype=torch.int32, device=q.device)
+        score = torch.empty((prob.n, prob.k), dtype=torch.float32, device=q.device)
+    else:
+        idx, score = out
+    st = Stats()
+    _check(lib.hytopk_select(ctypes.byref(prob), ctypes.byref(prm) if prm else None, _ptr(q),
+                             _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), _ptr(idx), _ptr(score),
+                             _ptr(workspace), workspace.numel(), _stream(q), ctypes.byref(st)))
+    return (idx, score, st.as_dict()) if with_stats else (idx, score)
+
+
+def replay(q, k, w, idx, *, q_scale=None, k_scale=None, q_start=None, out=None):
+    """Selection replay: scores of the saved indices idx [n][k] (-inf at idx < 0)."""
+    import torch
+    lib = load_library()
+    prob = _problem(q, k, w, idx.shape[1], q_start)
+    if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.shape[0] != prob.n:
+        raise ValueError("idx must be a contiguous int32 [n][k] tensor")
+    if out is None:
+        out = torch.empty(idx.shape, dtype=torch.float32, device=q.device)
+    _check(lib.hytopk_replay(ctypes.byref(prob), _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale),
+                             _ptr(w), _ptr(idx), _ptr(out), _stream(q)))
+    return out
+
+
+def baseline_select(q, k, w, topk: int, *, q_scale=None, k_scale=None, q_start=None,
+                    workspace=None, out=None):
+    """The materialise-then-top-k route (writes the n x L fp32 score table)."""
+    import torch
+    lib = load_library()
+    prob = _problem(q, k, w, topk, q_start)
+    need = int(lib.hytopk_baseline_workspace(ctypes.byref(prob)))
+    if workspace is None:
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if out is None:
+        idx = torch.empty((prob.n, prob.k), dtype=torch.int32, device=q.device)
+        score = torch.empty((prob.n, prob.k), dtype=torch.float32, device=q.device)
+    else:
+        idx, score = out
+    _check(lib.hytopk_baseline_select(ctypes.byref(prob), _ptr(q), _ptr(q_scale), _ptr(k),
+                                      _ptr(k_scale), _ptr(w), _ptr(idx), _ptr(score),
+                                      _ptr(workspace), workspace.numel(), _stream(q)))
+    return idx, score

@@ -1,0 +1,445 @@
+// C ABI of the selection library: argument validation, workspace layout and
+// the launch sequence of hytopk_select / hytopk_replay /
+// hytopk_baseline_select (declared in include/hytopk.h).
+#include <hip/hip_runtime.h>
+
+#include <algorithm>
+#include <cstdio>
+#include <cstring>
+#include <map>
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "hytopk.h"
+#include "launch.h"
+
+namespace {
+
+thread_local std::string g_err;
+
+int fail(int code, const char* msg) {
+  g_err = msg;
+  return code;
+}
+
+int hip_fail(hipError_t e, const char* where) {
+  g_err = std::string(where) + ": " + hipGetErrorString(e);
+  return HYTOPK_EHIP;
+}
+
+#define HK_HIP(expr, where)                     \
+  do {                                          \
+    hipError_t e_ = (expr);                     \
+    if (e_ != hipSuccess) return hip_fail(e_, where); \
+  } while (0)
+
+// ------------------------------------------------------------------ tracing
+
+struct TraceRec {
+  std::string name;
+  hipEvent_t a, b;
+};
+
+struct Tracer {
+  std::mutex mu;
+  bool on = false;
+  std::vector<TraceRec> pending;
+  std::vector<hipEvent_t> pool;
+  std::map<std::string, std::pair<int, double>> acc;
+};
+
+Tracer& tracer() {
+  static Tracer t;
+  return t;
+}
+
+hipEvent_t take_event(Tracer& t) {
+  if (!t.pool.empty()) {
+    hipEvent_t e = t.pool.back();
+    t.pool.pop_back();
+    return e;
+  }
+  hipEvent_t e = nullptr;
+  if (hipEventCreate(&e) != hipSuccess) return nullptr;
+  return e;
+}
+
+// Brackets one launch with events when tracing is on.
+struct Span {
+  const char* name;
+  hipStream_t s;
+  hipEvent_t a = nullptr;
+  Span(const char* nm, hipStream_t st) : name(nm), s(st) {
+    Tracer& t = tracer();
+    std::lock_guard<std::mutex> g(t.mu);
+    if (!t.on) return;
+    a = take_event(t);
+    if (a) hipEventRecord(a, s);
+  }
+  ~Span() {
+    if (!a) return;
+    Tracer& t = tracer();
+    std::lock_guard<std::mutex> g(t.mu);
+    hipEvent_t b = take_event(t);
+    if (!b) return;
+    hipEventRecord(b, s);
+    t.pending.push_back(TraceRec{name, a, b});
+  }
+};
+
+constexpr size_t kAlign = 256;
+constexpr int kMaxK = 2048;
+constexpr int kMaxCap = 16384;
+constexpr int kMaxM = 16384;
+constexpr size_t kLdsLimit = 160 * 1024 - 8 * 1024;  // gfx950 LDS minus static scratch
+
+size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
+
+struct Params {
+  int m_min, m_max, m_div, oversample, cap, max_recover, force_path, rows_chunk;
+};
+
+int check_problem(const hytopk_problem* p) {
+  if (!p) return fail(HYTOPK_EINVAL, "problem is NULL");
+  if (p->L <= 0 || p->n <= 0 || p->q_start < 0) return fail(HYTOPK_EINVAL, "L, n must be > 0 and q_start >= 0");
+  if (p->q_start + p->n > p->L) return fail(HYTOPK_EINVAL, "q_start + n > L");
+  if (p->L >= (int64_t(1) << 31)) return fail(HYTOPK_EUNSUPPORTED, "L >= 2^31");
+  if (p->k <= 0) return fail(HYTOPK_EINVAL, "k must be > 0");
+  if (p->k > kMaxK) return fail(HYTOPK_EUNSUPPORTED, "k > 2048");
+  if (p->H <= 0 || p->d <= 0) return fail(HYTOPK_EINVAL, "H, d must be > 0");
+  if (p->H > 64) return fail(HYTOPK_EUNSUPPORTED, "H > 64");
+  if (p->dtype == HYTOPK_BF16) {
+    if (p->d != 64 && p->d != 128) return fail(HYTOPK_EUNSUPPORTED, "bf16 needs d in {64, 128}");
+  } else if (p->dtype == HYTOPK_FP8_E4M3) {
+    if (p->d != 128) return fail(HYTOPK_EUNSUPPORTED, "fp8 needs d = 128");
+  } else {
+    return fail(HYTOPK_EINVAL, "unknown dtype");
+  }
+  return HYTOPK_OK;
+}
+
+Params resolve(const hytopk_problem* p, const hytopk_params* prm) {
+  Params r{};
+  r.m_min = (prm && prm->m_min) ? prm->m_min : 4096;
+  r.m_max = (prm && prm->m_max) ? prm->m_max : 8192;
+  r.m_div = (prm && prm->m_div) ? prm->m_div : 128;
+  r.oversample = (prm && prm->oversample) ? prm->oversample : 3;
+  r.cap = (prm && prm->cap) ? prm->cap : 6 * p->k;
+  r.max_recover = (prm && prm->max_recover) ? prm->max_recover : 64;
+  r.force_path = prm ? prm->force_path : HYTOPK_PATH_AUTO;
+  int64_t dflt = std::max<int64_t>(r.max_recover, (int64_t(1) << 29) / p->L);
+  dflt = std::min<int64_t>(dflt, p->n);
+  r.rows_chunk = (prm && prm->rows_chunk) ? prm->rows_chunk : (int)std::max<int64_t>(1, dflt);
+  return r;
+}
+
+int check_params(const hytopk_problem* p, const Params& r) {
+  if (r.m_min < 1 || r.m_max < r.m_min || r.m_div < 1 || r.oversample < 1 || r.cap < 1 ||
+      r.max_recover < 0 || r.rows_chunk < 1)
+    return fail(HYTOPK_EINVAL, "invalid threshold parameters");
+  if (r.force_path != HYTOPK_PATH_AUTO && r.force_path != HYTOPK_PATH_ROWS_ALL)
+    return fail(HYTOPK_EINVAL, "unknown force_path");
+  if (r.m_max > kMaxM) return fail(HYTOPK_EUNSUPPORTED, "m_max > 16384");
+  if (r.cap > kMaxCap) return fail(HYTOPK_EUNSUPPORTED, "cap > 16384");
+  if (hk::cand_select_lds_bytes(r.cap, p->k) > kLdsLimit)
+    return fail(HYTOPK_EUNSUPPORTED, "cap and k exceed the LDS of one workgroup");
+  return HYTOPK_OK;
+}
+
+int sample_count(const hytopk_problem* p, const Params& r) {
+  int64_t m = std::max<int64_t>(r.m_min, p->L / r.m_div);
+  return (int)std::min<int64_t>(m, r.m_max);
+}
+
+struct Layout {
+  size_t tau, cnt, failed, stats, cand, rows, total;
+  int rows_n;
+};
+
+Layout layout(const hytopk_problem* p, const Params& r) {
+  Layout l{};
+  size_t off = 0;
+  const size_t n = (size_t)p->n;
+  l.tau = off; off = align_up(off + n * 4);
+  l.cnt = off; off = align_up(off + n * 4);
+  l.failed = off; off = align_up(off + n * 4);
+  l.stats = off; off = align_up(off + sizeof(hk::DevStats));
+  l.cand = off; off = align_up(off + n * (size_t)r.cap * 8);
+  l.rows_n = std::max(r.max_recover, std::min(r.rows_chunk, (int)p->n));
+  l.rows = off; off = align_up(off + (size_t)l.rows_n * (size_t)p->L * 4);
+  l.total = off;
+  return l;
+}
+
+int check_ws(void* ws, size_t bytes, size_t need) {
+  if (!ws) return fail(HYTOPK_EWORKSPACE, "workspace is NULL");
+  if (reinterpret_cast<uintptr_t>(ws) % kAlign) return fail(HYTOPK_EWORKSPACE, "workspace not 256-byte aligned");
+  if (bytes < need) return fail(HYTOPK_EWORKSPACE, "workspace too small");
+  return HYTOPK_OK;
+}
+
+int check_inputs(const hytopk_problem* p, const void* q, const float* qs, const void* k,
+                 const float* ks, const float* w) {
+  if (!q || !k || !w) return fail(HYTOPK_EINVAL, "q, k and w must be non-NULL");
+  if (p->dtype == HYTOPK_FP8_E4M3 && (!qs || !ks))
+    return fail(HYTOPK_EINVAL, "fp8 needs q_scale and k_scale");
+  return HYTOPK_OK;
+}
+
+// Splits of the key range so that the score launch has enough workgroups.
+void splits(int64_t nq, int64_t maxctx, int& nsplit, int& split_len) {
+  const int64_t groups = (nq + 15) / 16;
+  int64_t want = (512 + groups - 1) / groups;
+  const int64_t most = std::max<int64_t>(1, (maxctx + 4095) / 4096);
+  want = std::max<int64_t>(1, std::min(want, most));
+  int64_t len = (maxctx + want - 1) / want;
+  len = (len + 63) / 64 * 64;
+  nsplit = (int)((maxctx + len - 1) / len);
+  split_len = (int)len;
+}
+
+hk::ScoreArgs score_args(const hytopk_problem* p, const void* q, const float* qs, const void* k,
+                         const float* ks, const float* w) {
+  hk::ScoreArgs a{};
+  a.q = static_cast<const uint8_t*>(q);
+  a.k = static_cast<const uint8_t*>(k);
+  a.w = w;
+  a.q_scale = qs;
+  a.k_scale = ks;
+  a.L = (int)p->L;
+  a.q_start = (int)p->q_start;
+  a.H = p->H;
+  return a;
+}
+
+// Score `nq` queries (qlist or q_offset..) into rows, then row top-k.
+int rows_path(const hytopk_problem* p, const hk::ScoreArgs& base, const int* qlist, int q_offset,
+              int nq, int64_t maxctx, float* rows, int32_t* out_idx, float* out_score,
+              hipStream_t s) {
+  hk::ScoreArgs a = base;
+  a.rows = rows;
+  a.row_stride = p->L;
+  a.qlist = qlist;
+  a.q_offset = q_offset;
+  a.nq = nq;
+  splits(nq, maxctx, a.nsplit, a.split_len);
+  const bool fp8 = p->dtype == HYTOPK_FP8_E4M3;
+  {
+    Span sp("score_rows", s);
+    HK_HIP(hk::launch_score(a, p->d, fp8, s), "score rows launch");
+  }
+  {
+    Span sp("row_topk", s);
+    HK_HIP(hk::launch_row_topk(rows, p->L, qlist, q_offset, nq, (int)p->q_start, p->k, (int)p->L,
+                               out_idx, out_score, s),
+           "row top-k launch");
+  }
+  return HYTOPK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* hytopk_status_string(int status) {
+  switch (status) {
+    case HYTOPK_OK: return "ok";
+    case HYTOPK_EINVAL: return "invalid argument";
+    case HYTOPK_EUNSUPPORTED: return "unsupported problem";
+    case HYTOPK_EWORKSPACE: return "bad workspace";
+    case HYTOPK_EHIP: return "HIP runtime error";
+    default: return "unknown status";
+  }
+}
+
+const char* hytopk_last_error(void) { return g_err.c_str(); }
+
+int hytopk_trace_enable(int on) {
+  Tracer& t = tracer();
+  std::lock_guard<std::mutex> g(t.mu);
+  const int prev = t.on ? 1 : 0;
+  t.on = on != 0;
+  if (t.on) t.acc.clear();
+  return prev;
+}
+
+int hytopk_trace_read(hytopk_trace_entry* out, int max) {
+  Tracer& t = tracer();
+  std::lock_guard<std::mutex> g(t.mu);
+  for (TraceRec& r : t.pending) {
+    hipError_t e = hipEventSynchronize(r.b);
+    if (e != hipSuccess) return hip_fail(e, "trace event sync");
+    float ms = 0.f;
+    e = hipEventElapsedTime(&ms, r.a, r.b);
+    if (e != hipSuccess) return hip_fail(e, "trace elapsed time");
+    auto& slot = t.acc[r.name];
+    slot.first += 1;
+    slot.second += ms;
+    t.pool.push_back(r.a);
+    t.pool.push_back(r.b);
+  }
+  t.pending.clear();
+  int i = 0;
+  for (const auto& kv : t.acc) {
+    if (out && i < max) {
+      std::memset(out[i].name, 0, sizeof(out[i].name));
+      std::strncpy(out[i].name, kv.first.c_str(), sizeof(out[i].name) - 1);
+      out[i].launches = kv.second.first;
+      out[i].total_ms = kv.second.second;
+    }
+    ++i;
+  }
+  return i;
+}
+
+size_t hytopk_select_workspace(const hytopk_problem* p, const hytopk_params* prm) {
+  if (check_problem(p) != HYTOPK_OK) return 0;
+  Params r = resolve(p, prm);
+  if (check_params(p, r) != HYTOPK_OK) return 0;
+  return layout(p, r).total;
+}
+
+size_t hytopk_baseline_workspace(const hytopk_problem* p) {
+  if (check_problem(p) != HYTOPK_OK) return 0;
+  return (size_t)p->n * (size_t)p->L * 4;
+}
+
+int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void* q,
+                  const float* q_scale, const void* k, const float* k_scale, const float* w,
+                  int32_t* out_idx, float* out_score, void* workspace, size_t workspace_bytes,
+                  void* stream, hytopk_stats* stats) {
+  g_err.clear();
+  int rc = check_problem(p);
+  if (rc) return rc;
+  Params r = resolve(p, prm);
+  if ((rc = check_params(p, r))) return rc;
+  if ((rc = check_inputs(p, q, q_scale, k, k_scale, w))) return rc;
+  if (!out_idx) return fail(HYTOPK_EINVAL, "out_idx is NULL");
+  const Layout l = layout(p, r);
+  if ((rc = check_ws(workspace, workspace_bytes, l.total))) return rc;
+
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  float* tau = reinterpret_cast<float*>(ws + l.tau);
+  int* cnt = reinterpret_cast<int*>(ws + l.cnt);
+  int* failed = reinterpret_cast<int*>(ws + l.failed);
+  hk::DevStats* dst = reinterpret_cast<hk::DevStats*>(ws + l.stats);
+  uint2* cand = reinterpret_cast<uint2*>(ws + l.cand);
+  float* rows = reinterpret_cast<float*>(ws + l.rows);
+  const bool fp8 = p->dtype == HYTOPK_FP8_E4M3;
+  const int n = (int)p->n;
+  const int64_t maxctx = p->q_start + p->n;
+  const hk::ScoreArgs base = score_args(p, q, q_scale, k, k_scale, w);
+
+  hk::DevStats hs{};
+  int path = 0;
+  if (r.force_path != HYTOPK_PATH_ROWS_ALL) {
+    HK_HIP(hk::launch_zero(cnt, n, dst, s), "zero launch");
+    hk::SampleArgs sa{};
+    sa.q = base.q; sa.k = base.k; sa.w = w; sa.q_scale = q_scale; sa.k_scale = k_scale;
+    sa.tau = tau; sa.L = (int)p->L; sa.q_start = (int)p->q_start; sa.n = n; sa.H = p->H;
+    sa.topk = p->k; sa.M = sample_count(p, r); sa.oversample = r.oversample;
+    {
+      Span sp("sample_tau", s);
+      HK_HIP(hk::launch_sample_tau(sa, p->d, fp8, s), "sample/threshold launch");
+    }
+
+    hk::ScoreArgs a = base;
+    a.tau = tau;
+    a.cnt = cnt;
+    a.cand = cand;
+    a.cap = r.cap;
+    a.nq = n;
+    splits(n, maxctx, a.nsplit, a.split_len);
+    {
+      Span sp("score_compact", s);
+      HK_HIP(hk::launch_score(a, p->d, fp8, s), "fused score launch");
+    }
+    {
+      Span sp("check", s);
+      HK_HIP(hk::launch_check(cnt, n, (int)p->q_start, p->k, r.cap, dst, failed, s), "check launch");
+    }
+    HK_HIP(hipMemcpyAsync(&hs, dst, sizeof(hs), hipMemcpyDeviceToHost, s), "stats copy");
+    HK_HIP(hipStreamSynchronize(s), "stream sync");
+    path = hs.n_failed > r.max_recover ? 1 : 0;
+  } else {
+    path = 2;
+  }
+
+  if (path == 0) {
+    {
+      Span sp("cand_select", s);
+      HK_HIP(hk::launch_cand_select(cnt, cand, n, (int)p->q_start, p->k, r.cap, (int)p->L, out_idx,
+                                    out_score, s),
+             "candidate select launch");
+    }
+    // Recovery: rescore only the flagged queries over their whole context.
+    for (int f0 = 0; f0 < hs.n_failed; f0 += l.rows_n) {
+      const int nf = std::min(l.rows_n, hs.n_failed - f0);
+      rc = rows_path(p, base, failed + f0, 0, nf, maxctx, rows, out_idx, out_score, s);
+      if (rc) return rc;
+    }
+  } else {
+    // Full rescore: every query through the row path, in chunks of rows_n.
+    for (int c0 = 0; c0 < n; c0 += l.rows_n) {
+      const int nc = std::min(l.rows_n, n - c0);
+      rc = rows_path(p, base, nullptr, c0, nc, p->q_start + c0 + nc, rows, out_idx, out_score, s);
+      if (rc) return rc;
+    }
+  }
+  if (stats) {
+    stats->n_overflow = hs.n_overflow;
+    stats->n_underk = hs.n_underk;
+    stats->n_failed = hs.n_failed;
+    stats->full_rescore = path != 0;
+    stats->cand_total = (int64_t)hs.cand_total;
+    stats->cand_max = hs.cand_max;
+    stats->path = path;
+  }
+  return HYTOPK_OK;
+}
+
+int hytopk_replay(const hytopk_problem* p, const void* q, const float* q_scale, const void* k,
+                  const float* k_scale, const float* w, const int32_t* idx, float* out_score,
+                  void* stream) {
+  g_err.clear();
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if ((rc = check_inputs(p, q, q_scale, k, k_scale, w))) return rc;
+  if (!idx || !out_score) return fail(HYTOPK_EINVAL, "idx and out_score must be non-NULL");
+  hk::ReplayArgs a{};
+  a.q = static_cast<const uint8_t*>(q);
+  a.k = static_cast<const uint8_t*>(k);
+  a.w = w;
+  a.q_scale = q_scale;
+  a.k_scale = k_scale;
+  a.idx = idx;
+  a.out = out_score;
+  a.L = (int)p->L;
+  a.n = (int)p->n;
+  a.H = p->H;
+  a.topk = p->k;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  Span sp("replay", s);
+  HK_HIP(hk::launch_replay(a, p->d, p->dtype == HYTOPK_FP8_E4M3, s), "replay launch");
+  return HYTOPK_OK;
+}
+
+int hytopk_baseline_select(const hytopk_problem* p, const void* q, const float* q_scale,
+                           const void* k, const float* k_scale, const float* w, int32_t* out_idx,
+                           float* out_score, void* workspace, size_t workspace_bytes,
+                           void* stream) {
+  g_err.clear();
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if ((rc = check_inputs(p, q, q_scale, k, k_scale, w))) return rc;
+  if (!out_idx) return fail(HYTOPK_EINVAL, "out_idx is NULL");
+  if ((rc = check_ws(workspace, workspace_bytes, hytopk_baseline_workspace(p)))) return rc;
+  const hk::ScoreArgs base = score_args(p, q, q_scale, k, k_scale, w);
+  return rows_path(p, base, nullptr, 0, (int)p->n, p->q_start + p->n,
+                   static_cast<float*>(workspace), out_idx, out_score,
+                   static_cast<hipStream_t>(stream));
+}
+
+}  // extern "C"

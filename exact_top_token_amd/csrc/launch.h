@@ -1,0 +1,109 @@
+// Internal host-side launch interface between the C ABI (api.hip) and the
+// kernel translation units.  Every launcher enqueues on `s` and returns the
+// hipError_t of the launch.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace hk {
+
+// Fused indexer scoring over causal key ranges.
+//   COMPACT (rows == nullptr): keys with score >= tau[q] go to the candidate
+//     buffer cand[q][0..cap) as {position, fp32 bits}; cnt[q] counts every
+//     passing key, including those beyond cap.
+//   ROWS (rows != nullptr): the score of every causal key is written to
+//     rows[e * row_stride + key] for launch entry e.
+// Launch entry e scores query qlist[e] (or q_offset + e when qlist is null).
+struct ScoreArgs {
+  const uint8_t* q;
+  const uint8_t* k;
+  const float* w;
+  const float* q_scale;
+  const float* k_scale;
+  const float* tau;
+  int* cnt;
+  uint2* cand;
+  float* rows;
+  const int* qlist;
+  int64_t row_stride;
+  int L;
+  int q_start;
+  int q_offset;
+  int nq;
+  int H;
+  int cap;
+  int nsplit;
+  int split_len;
+};
+
+hipError_t launch_score(const ScoreArgs& a, int d, bool fp8, hipStream_t s);
+
+// Per-query sampled threshold: tau[q] = the r-th largest of the M_q sample
+// scores at positions floor(j * ctx / M_q).
+struct SampleArgs {
+  const uint8_t* q;
+  const uint8_t* k;
+  const float* w;
+  const float* q_scale;
+  const float* k_scale;
+  float* tau;
+  int L;
+  int q_start;
+  int n;
+  int H;
+  int topk;
+  int M;
+  int oversample;
+};
+
+hipError_t launch_sample_tau(const SampleArgs& a, int d, bool fp8, hipStream_t s);
+
+// Replay: out[q][j] = I(q_start + q, idx[q][j]) (-inf where idx is outside [0, L)).
+struct ReplayArgs {
+  const uint8_t* q;
+  const uint8_t* k;
+  const float* w;
+  const float* q_scale;
+  const float* k_scale;
+  const int* idx;
+  float* out;
+  int L;
+  int n;
+  int H;
+  int topk;
+};
+
+hipError_t launch_replay(const ReplayArgs& a, int d, bool fp8, hipStream_t s);
+
+// Device counters of one selection call.
+struct DevStats {
+  int n_overflow;
+  int n_underk;
+  int n_failed;
+  int cand_max;
+  unsigned long long cand_total;
+  int pad[2];
+};
+
+hipError_t launch_zero(int* cnt, int n, DevStats* st, hipStream_t s);
+
+// Check: flags queries whose candidate count is above cap or below
+// min(k, ctx) and appends them to `failed`.
+hipError_t launch_check(const int* cnt, int n, int q_start, int topk, int cap, DevStats* st,
+                        int* failed, hipStream_t s);
+
+// Exact top-k of each passing query's candidates (failed queries are skipped).
+hipError_t launch_cand_select(const int* cnt, const uint2* cand, int n, int q_start, int topk,
+                              int cap, int L, int* out_idx, float* out_score, hipStream_t s);
+
+// Exact top-k of score rows: entry e is row rows[e * row_stride] of query
+// qlist[e] (or q_offset + e).
+hipError_t launch_row_topk(const float* rows, int64_t row_stride, const int* qlist, int q_offset,
+                           int nq, int q_start, int topk, int L, int* out_idx, float* out_score,
+                           hipStream_t s);
+
+// LDS bytes cand_select needs for this cap / k (the host checks the limit).
+size_t cand_select_lds_bytes(int cap, int topk);
+
+}  // namespace hk

@@ -1,0 +1,361 @@
+// Check, exact selection and ordering ("HyScale sparse-attention training --
+// Selection without a score table", HyTopK paragraph).
+//
+// * check: a query fails when its candidates overflowed the buffer (count >
+//   cap) or number fewer than min(k, ctx).
+// * cand_select: for every query that passed, the exact top-k of its
+//   candidates.  Candidates arrive in whatever order the atomic flushes left
+//   them, so every step below depends only on the candidate multiset, which
+//   makes the output bitwise reproducible:
+//     1. radix select of the k-th largest order-preserving score key;
+//     2. at that score, radix select over positions keeps the lowest-position
+//        ties ("resolves ties at the k-th score with a radix select over
+//        positions");
+//     3. LSD radix sort of the kept k by (score descending, position
+//        ascending) ("orders the k kept entries with a radix sort").
+// * row_topk: the same result from materialised score rows (the conventional
+//   two-kernel route, recovery and full rescore): radix select over the row,
+//   emission of the kept entries in position order (ties: first ones win),
+//   then a stable radix sort by score descending.
+#include "common.h"
+#include "launch.h"
+
+namespace hk {
+
+constexpr int kSelThreads = 512;
+constexpr int kSelWaves = kSelThreads / kWave;
+constexpr int kMaxRounds = 8;  // k <= 4096 = kMaxRounds * kSelThreads
+
+// ----------------------------------------------------------------- helpers
+
+struct SortScratch {
+  int cnt[16][kMaxRounds][kSelWaves];  // per (digit, round, wave) counts, then offsets
+  int wsum[kSelWaves];
+  int skip;
+};
+
+// Exclusive scan, in place, of `m` ints of `v` (m <= 2 * kSelThreads).
+__device__ void block_scan_excl(int* v, int m, int* wsum) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int i0 = 2 * tid, i1 = 2 * tid + 1;
+  const int a0 = i0 < m ? v[i0] : 0;
+  const int a1 = i1 < m ? v[i1] : 0;
+  const int loc = a0 + a1;
+  const int pre = wave_prefix_excl(loc);
+  if (lane == kWave - 1) wsum[wave] = pre + loc;
+  __syncthreads();
+  int base = 0;
+  for (int w = 0; w < wave; ++w) base += wsum[w];
+  if (i0 < m) v[i0] = base + pre;
+  if (i1 < m) v[i1] = base + pre + a0;
+  __syncthreads();
+}
+
+// Stable LSD radix sort, ascending by key bits [lo, hi) in 4-bit digits, of
+// the N (key, val) pairs in (k0, v0); (k1, v1) is scratch of the same size.
+// Returns true when the result ended in (k1, v1).
+__device__ bool block_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int N,
+                                 int lo, int hi, SortScratch& ss) {
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int rounds = (N + kSelThreads - 1) / kSelThreads;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  bool flipped = false;
+  for (int sh = lo; sh < hi; sh += 4) {
+    int myd[kMaxRounds], myrank[kMaxRounds];
+#pragma unroll
+    for (int j = 0; j < kMaxRounds; ++j) {
+      if (j >= rounds) break;
+      const int i = j * kSelThreads + tid;
+      const bool ok = i < N;
+      const int d = ok ? (int)((k0[i] >> sh) & 15u) : 16;
+      int rank = 0;
+      for (int b = 0; b < 16; ++b) {
+        const uint64_t mb = __ballot(d == b);
+        if (d == b) rank = __popcll(mb & lt);
+        if (lane == 0) ss.cnt[b][j][wave] = __popcll(mb);
+      }
+      myd[j] = d;
+      myrank[j] = rank;
+    }
+    if (tid == 0) ss.skip = 0;
+    __syncthreads();
+    // A pass whose digit is the same for all N entries leaves the order alone.
+    if (tid < 16) {
+      int tot = 0;
+      for (int j = 0; j < rounds; ++j)
+        for (int w = 0; w < kSelWaves; ++w) tot += ss.cnt[tid][j][w];
+      if (tot == N) ss.skip = 1;
+    }
+    __syncthreads();
+    const bool skip = ss.skip != 0;
+    __syncthreads();  // everyone has read the flag before thread 0 resets it
+    if (skip) continue;  // uniform
+    // Offsets in (digit, round, wave) order; unused rounds hold zero counts.
+    for (int b = tid; b < 16 * kMaxRounds * kSelWaves; b += kSelThreads) {
+      const int j = (b / kSelWaves) % kMaxRounds;
+      if (j >= rounds) (&ss.cnt[0][0][0])[b] = 0;
+    }
+    __syncthreads();
+    block_scan_excl(&ss.cnt[0][0][0], 16 * kMaxRounds * kSelWaves, ss.wsum);
+#pragma unroll
+    for (int j = 0; j < kMaxRounds; ++j) {
+      if (j >= rounds) break;
+      const int i = j * kSelThreads + tid;
+      if (i < N) {
+        const int dst = ss.cnt[myd[j]][j][wave] + myrank[j];
+        k1[dst] = k0[i];
+        v1[dst] = v0[i];
+      }
+    }
+    __syncthreads();
+    uint32_t* t;
+    t = k0; k0 = k1; k1 = t;
+    t = v0; v0 = v1; v1 = t;
+    flipped = !flipped;
+  }
+  return flipped;
+}
+
+__device__ __forceinline__ int bits_for(int L) {
+  int b = 0;
+  while ((1 << b) < L && b < 31) ++b;
+  return (b + 3) & ~3;
+}
+
+// ----------------------------------------------------------------- zero / check
+
+__global__ void zero_kernel(int* cnt, int n, DevStats* st) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) cnt[i] = 0;
+  if (i == 0) {
+    st->n_overflow = 0;
+    st->n_underk = 0;
+    st->n_failed = 0;
+    st->cand_max = 0;
+    st->cand_total = 0ull;
+  }
+}
+
+hipError_t launch_zero(int* cnt, int n, DevStats* st, hipStream_t s) {
+  const int nb = (n + 255) / 256;
+  hipLaunchKernelGGL(zero_kernel, dim3(nb > 0 ? nb : 1), dim3(256), 0, s, cnt, n, st);
+  return hipGetLastError();
+}
+
+__global__ void check_kernel(const int* cnt, int n, int q_start, int topk, int cap, DevStats* st,
+                             int* failed) {
+  const int i = blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n) return;
+  const int c = cnt[i];
+  const int ctx = q_start + i + 1;
+  const int need = min(topk, ctx);
+  const bool over = c > cap, under = c < need;
+  atomicAdd(&st->cand_total, (unsigned long long)c);
+  atomicMax(&st->cand_max, c);
+  if (over) atomicAdd(&st->n_overflow, 1);
+  if (under) atomicAdd(&st->n_underk, 1);
+  if (over || under) failed[atomicAdd(&st->n_failed, 1)] = i;
+}
+
+hipError_t launch_check(const int* cnt, int n, int q_start, int topk, int cap, DevStats* st,
+                        int* failed, hipStream_t s) {
+  hipLaunchKernelGGL(check_kernel, dim3((n + 255) / 256), dim3(256), 0, s, cnt, n, q_start, topk,
+                     cap, st, failed);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- output
+
+// Sort the `need` selected (key, pos) pairs by (score desc, pos asc) and write
+// the output row; entries need..topk-1 are padding.  pos_sorted: the pairs
+// are already in ascending position order, so a stable sort by score suffices.
+__device__ void sort_and_emit(uint32_t* sk, uint32_t* sp, uint32_t* tk, uint32_t* tp, int need,
+                              int topk, int L, bool pos_sorted, int* out_idx, float* out_score,
+                              SortScratch& ss) {
+  const int tid = threadIdx.x;
+  // Ascending by (~key, pos): LSD, position bits first.
+  for (int i = tid; i < need; i += kSelThreads) sk[i] = ~sk[i];
+  __syncthreads();
+  bool fl = false;
+  if (!pos_sorted) {
+    // sort by position: use the position as the key temporarily
+    fl = block_sort_pairs(sp, sk, tp, tk, need, 0, bits_for(L), ss);
+    if (fl) { uint32_t* t = sk; sk = tk; tk = t; t = sp; sp = tp; tp = t; }
+  }
+  fl = block_sort_pairs(sk, sp, tk, tp, need, 0, 32, ss);
+  if (fl) { sk = tk; sp = tp; }
+  for (int i = tid; i < topk; i += kSelThreads) {
+    if (i < need) {
+      out_idx[i] = (int)sp[i];
+      if (out_score) out_score[i] = key_score(~sk[i]);
+    } else {
+      out_idx[i] = -1;
+      if (out_score) out_score[i] = -__builtin_inff();
+    }
+  }
+}
+
+// ----------------------------------------------------------------- candidates
+
+struct CandShared {
+  RadixScratch rs;
+  SortScratch ss;
+  int nsel;
+};
+
+size_t cand_select_lds_bytes(int cap, int topk) {
+  // candidates (key + pos) followed by the selected pairs (key + pos)
+  return (size_t)cap * 8 + (size_t)topk * 8;
+}
+
+__global__ void __launch_bounds__(kSelThreads) cand_select_kernel(const int* cnt, const uint2* cand,
+                                                                  int q_start, int topk, int cap,
+                                                                  int L, int* out_idx,
+                                                                  float* out_score) {
+  extern __shared__ uint32_t dyn[];
+  __shared__ CandShared sh;
+  const int q = blockIdx.x, tid = threadIdx.x;
+  const int c = cnt[q];
+  const int ctx = q_start + q + 1;
+  const int need = min(topk, ctx);
+  if (c > cap || c < need) return;  // failed: recovered on the row path
+  uint32_t* ck = dyn;               // [cap] score keys
+  uint32_t* cp = dyn + cap;         // [cap] positions
+  uint32_t* sk = dyn + 2 * cap;     // [topk] selected keys
+  uint32_t* sp = sk + topk;         // [topk] selected positions
+  const uint2* src = cand + (int64_t)q * cap;
+  for (int i = tid; i < c; i += kSelThreads) {
+    const uint2 e = src[i];
+    cp[i] = e.x;
+    ck[i] = score_key(__uint_as_float(e.y));
+  }
+  if (tid == 0) sh.nsel = 0;
+  __syncthreads();
+  int rem;
+  const uint32_t v = block_select_largest(
+      c, need, [&](int i) { return ck[i]; }, [](int) { return true; }, sh.rs, rem);
+  // rem = how many entries equal to v belong to the top k: keep the rem
+  // lowest positions among them (position select: largest of ~pos).
+  uint32_t pmax = 0xFFFFFFFFu;
+  {
+    int mult = 0;
+    if (tid == 0) sh.rs.rank = 0;
+    __syncthreads();
+    int loc = 0;
+    for (int i = tid; i < c; i += kSelThreads) loc += (ck[i] == v);
+    if (loc) atomicAdd(&sh.rs.rank, loc);
+    __syncthreads();
+    mult = sh.rs.rank;
+    __syncthreads();
+    if (rem < mult) {
+      int rr;
+      pmax = ~block_select_largest(
+          c, rem, [&](int i) { return ~cp[i]; }, [&](int i) { return ck[i] == v; }, sh.rs, rr);
+    }
+  }
+  for (int i = tid; i < c; i += kSelThreads) {
+    const uint32_t kk = ck[i];
+    if (kk > v || (kk == v && cp[i] <= pmax)) {
+      const int slot = atomicAdd(&sh.nsel, 1);
+      if (slot < need) {  // exactly `need` entries qualify; the guard keeps LDS writes in bounds
+        sk[slot] = kk;
+        sp[slot] = cp[i];
+      }
+    }
+  }
+  __syncthreads();
+  // The candidate area is free now: use it as the sort's scratch.
+  sort_and_emit(sk, sp, ck, cp, need, topk, L, false, out_idx + (int64_t)q * topk,
+                out_score ? out_score + (int64_t)q * topk : nullptr, sh.ss);
+}
+
+hipError_t launch_cand_select(const int* cnt, const uint2* cand, int n, int q_start, int topk,
+                              int cap, int L, int* out_idx, float* out_score, hipStream_t s) {
+  const size_t lds = cand_select_lds_bytes(cap, topk);
+  hipError_t e = hipFuncSetAttribute((const void*)cand_select_kernel,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(cand_select_kernel, dim3((unsigned)n), dim3(kSelThreads), lds, s, cnt, cand,
+                     q_start, topk, cap, L, out_idx, out_score);
+  return hipGetLastError();
+}
+
+// ----------------------------------------------------------------- score rows
+
+struct RowShared {
+  RadixScratch rs;
+  SortScratch ss;
+  int gt[kSelWaves];
+  int eq[kSelWaves];
+  uint32_t sk[2][4096];
+  uint32_t sp[2][4096];
+};
+
+__global__ void __launch_bounds__(kSelThreads) row_topk_kernel(const float* rows, int64_t row_stride,
+                                                               const int* qlist, int q_offset,
+                                                               int q_start, int topk, int L,
+                                                               int* out_idx, float* out_score) {
+  __shared__ RowShared sh;
+  const int e = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int q = qlist ? qlist[e] : q_offset + e;
+  const int ctx = q_start + q + 1;
+  const int need = min(topk, ctx);
+  const float* row = rows + (int64_t)e * row_stride;
+  int rem;
+  const uint32_t v = block_select_largest(
+      ctx, need, [&](int i) { return score_key(row[i]); }, [](int) { return true; }, sh.rs, rem);
+  // Emit in position order: every key > v, and the first `rem` keys == v.
+  const int seg = ((ctx + kSelWaves - 1) / kSelWaves + kWave - 1) / kWave * kWave;
+  const int s0 = min(ctx, wave * seg), s1 = min(ctx, s0 + seg);
+  int ngt = 0, neq = 0;
+  for (int i = s0 + lane; i < s1; i += kWave) {
+    const uint32_t kk = score_key(row[i]);
+    ngt += kk > v;
+    neq += kk == v;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    ngt += __shfl_xor(ngt, off);
+    neq += __shfl_xor(neq, off);
+  }
+  if (lane == 0) { sh.gt[wave] = ngt; sh.eq[wave] = neq; }
+  __syncthreads();
+  int gt_before = 0, eq_before = 0;
+  for (int w = 0; w < wave; ++w) { gt_before += sh.gt[w]; eq_before += sh.eq[w]; }
+  int out = gt_before + min(eq_before, rem);  // kept entries before this segment
+  int ties = eq_before;                         // ties before the current element
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int i0 = s0; i0 < s1; i0 += kWave) {
+    const int i = i0 + lane;
+    const uint32_t kk = i < s1 ? score_key(row[i]) : 0u;
+    const bool isgt = i < s1 && kk > v;
+    const bool iseq = i < s1 && kk == v;
+    const uint64_t meq = __ballot(iseq);
+    const int tie_rank = ties + __popcll(meq & lt);
+    const bool keep = isgt || (iseq && tie_rank < rem);
+    const uint64_t mk = __ballot(keep);
+    if (keep) {
+      const int slot = out + __popcll(mk & lt);
+      if (slot < need) {  // exactly `need` entries qualify; the guard keeps LDS writes in bounds
+        sh.sk[0][slot] = kk;
+        sh.sp[0][slot] = (uint32_t)i;
+      }
+    }
+    out += __popcll(mk);
+    ties += __popcll(meq);
+  }
+  __syncthreads();
+  sort_and_emit(sh.sk[0], sh.sp[0], sh.sk[1], sh.sp[1], need, topk, L, true,
+                out_idx + (int64_t)q * topk, out_score ? out_score + (int64_t)q * topk : nullptr,
+                sh.ss);
+}
+
+hipError_t launch_row_topk(const float* rows, int64_t row_stride, const int* qlist, int q_offset,
+                           int nq, int q_start, int topk, int L, int* out_idx, float* out_score,
+                           hipStream_t s) {
+  if (nq <= 0) return hipSuccess;
+  hipLaunchKernelGGL(row_topk_kernel, dim3((unsigned)nq), dim3(kSelThreads), 0, s, rows,
+                     row_stride, qlist, q_offset, q_start, topk, L, out_idx, out_score);
+  return hipGetLastError();
+}
+
+}  // namespace hk

@@ -1,0 +1,200 @@
+// Fused indexer scoring over causal key ranges (the hot loop of HyTopK).
+//
+// A workgroup of 8 waves owns 16 queries (8 query pairs, one pair per wave,
+// queries held in registers as MFMA A operands) and streams key tiles of 64
+// keys through LDS; every key tile is read from memory once per 16 queries.
+// Per 16-key column block each wave runs 8 x 4 MFMAs (bf16, H = 64, d = 128),
+// applies ReLU and the weighted head sum in registers and then either
+//   COMPACT: compares each score with the query's sampled threshold and
+//     appends the passing keys to a per-wave LDS staging area; full stages are
+//     flushed with one atomicAdd on the query's global candidate counter and
+//     a copy into the candidate buffer ("compares each score with the
+//     threshold on chip and writes only the keys that pass into a small
+//     candidate buffer": HyScale explainer, HyTopK paragraph);
+//   ROWS: writes the score to a full score row (the conventional table of the
+//     explainer's contest paragraph; also the recovery and full-rescore path).
+// Both modes share the scoring code, so a query's scores are bit-identical on
+// every path.
+#include "launch.h"
+#include "tile.h"
+
+namespace hk {
+
+constexpr int kTK = 64;          // keys per LDS tile
+constexpr int kThreads = 512;    // 8 waves = 8 query pairs
+constexpr int kSB = 128;         // staged candidates per query before a flush
+
+template <int RB, int D, bool FP8, bool ROWS>
+__global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
+  using T = PairTile<RB, D, FP8>;
+  using Frag = typename T::Frag;
+  constexpr int RBYTES = T::RBYTES, NCH = T::NCH, KS = T::KS, FB = T::FB;
+  constexpr int TILE_BYTES = kTK * RBYTES;
+  constexpr int PER = kTK * NCH / kThreads;  // 16-byte chunks each thread stages per tile
+  static_assert((kTK * NCH) % kThreads == 0, "tile must split evenly over the workgroup");
+
+  __shared__ __attribute__((aligned(16))) uint8_t tile[2][TILE_BYTES];
+  __shared__ uint2 stage[ROWS ? 1 : 8][2][kSB];
+  __shared__ int s_maxt[8];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4;
+  const int group = blockIdx.x / a.nsplit, split = blockIdx.x % a.nsplit;
+  const int e0 = group * 16 + wave * 2;
+  const int ea = e0 < a.nq ? e0 : -1;
+  const int eb = e0 + 1 < a.nq ? e0 + 1 : -1;
+  const int qa = ea < 0 ? -1 : (a.qlist ? a.qlist[ea] : a.q_offset + ea);
+  const int qb = eb < 0 ? -1 : (a.qlist ? a.qlist[eb] : a.q_offset + eb);
+
+  if (lane == 0) {
+    int m = -1;
+    if (qa >= 0) m = a.q_start + qa;
+    if (qb >= 0) m = max(m, a.q_start + qb);
+    s_maxt[wave] = m;
+  }
+  __syncthreads();
+  int maxt = s_maxt[0];
+#pragma unroll
+  for (int w = 1; w < 8; ++w) maxt = max(maxt, s_maxt[w]);
+  const int kb = split * a.split_len;
+  const int ke = min(kb + a.split_len, maxt + 1);
+  if (kb >= ke) return;  // uniform over the workgroup
+  const int ntiles = (ke - kb + kTK - 1) / kTK;
+
+  T qt;
+  qt.load(a.q, a.w, a.q_scale, a.H, qa, qb);
+
+  // This lane's query (lanes 0..31: A, 32..63: B) and its key limit.
+  const int sel = lane >> 5;
+  const int qs = sel ? qb : qa;
+  const int es = sel ? eb : ea;
+  const int lim = qs >= 0 ? min(a.q_start + qs + 1, ke) : 0;
+  float tau = 0.0f;
+  if (!ROWS) tau = qs >= 0 ? a.tau[qs] : 0.0f;
+  const bool owner = (lane & 16) == 0;  // lanes 0..15 and 32..47 own distinct (query, key)
+
+  int cntA = 0, cntB = 0;  // staged candidates (wave-uniform)
+
+  auto flush = [&](int which, int count) {
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+    const int qf = which ? qb : qa;
+    int base = 0;
+    if (lane == 0) base = atomicAdd(a.cnt + qf, count);
+    base = __shfl(base, 0);
+    uint2* dst = a.cand + (int64_t)qf * a.cap;
+    for (int j = lane; j < count; j += kWave) {
+      const int p = base + j;
+      if (p < a.cap) dst[p] = stage[ROWS ? 0 : wave][which][j];
+    }
+    __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
+    __builtin_amdgcn_wave_barrier();
+  };
+
+  u32x4 pre[PER];
+  auto gload = [&](int k0) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = tid + p * kThreads;
+      const int kk = idx / NCH, c = idx % NCH;
+      const int gk = k0 + kk;
+      if (gk < a.L) {
+        pre[p] = *reinterpret_cast<const u32x4*>(a.k + (int64_t)gk * RBYTES + c * 16);
+      } else {
+        pre[p] = u32x4{0u, 0u, 0u, 0u};
+      }
+    }
+  };
+  auto lstore = [&](int buf) {
+#pragma unroll
+    for (int p = 0; p < PER; ++p) {
+      const int idx = tid + p * kThreads;
+      const int kk = idx / NCH, c = idx % NCH;
+      *reinterpret_cast<u32x4*>(&tile[buf][kk * RBYTES + ((c ^ (kk & (NCH - 1))) * 16)]) = pre[p];
+    }
+  };
+
+  gload(kb);
+  lstore(0);
+  __syncthreads();
+
+  for (int it = 0; it < ntiles; ++it) {
+    const int k0 = kb + it * kTK;
+    const int buf = it & 1;
+    if (it + 1 < ntiles) gload(k0 + kTK);
+    const uint8_t* tb = tile[buf];
+#pragma unroll
+    for (int cb = 0; cb < kTK / 16; ++cb) {
+      const int kt = cb * 16 + (lane & 15);
+      Frag b[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        if constexpr (FP8) {
+          const int c0 = 2 * (4 * ks + g);
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(tb + kt * RBYTES + ((c0 ^ (kt & (NCH - 1))) * 16));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(tb + kt * RBYTES + (((c0 + 1) ^ (kt & (NCH - 1))) * 16));
+          b[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                        (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+        } else {
+          const int c = 4 * ks + g;
+          b[ks] = *reinterpret_cast<const bf16x8*>(tb + kt * RBYTES + ((c ^ (kt & (NCH - 1))) * 16));
+        }
+      }
+      const int key = k0 + kt;
+      float s = qt.score(b);
+      if constexpr (FP8) s *= (key < a.L) ? a.k_scale[key] : 0.0f;
+      const bool inrange = owner && key < lim;
+      if constexpr (ROWS) {
+        if (inrange) a.rows[(int64_t)es * a.row_stride + key] = s;
+      } else {
+        const bool pass = inrange && s >= tau;
+        const uint64_t m = __ballot(pass);
+        if (m) {
+          const uint32_t mA = (uint32_t)(m & 0xFFFFull);
+          const uint32_t mB = (uint32_t)((m >> 32) & 0xFFFFull);
+          if (pass) {
+            const uint32_t mm = sel ? mB : mA;
+            const int rank = __popc(mm & ((1u << (lane & 15)) - 1u));
+            const int slot = (sel ? cntB : cntA) + rank;
+            stage[wave][sel][slot] = make_uint2((uint32_t)key, __float_as_uint(s));
+          }
+          cntA += __popc(mA);
+          cntB += __popc(mB);
+          if (cntA > kSB - 16) { flush(0, cntA); cntA = 0; }
+          if (cntB > kSB - 16) { flush(1, cntB); cntB = 0; }
+        }
+      }
+    }
+    if (it + 1 < ntiles) lstore(buf ^ 1);
+    __syncthreads();
+  }
+  if constexpr (!ROWS) {
+    if (cntA > 0) flush(0, cntA);
+    if (cntB > 0) flush(1, cntB);
+  }
+}
+
+template <int RB, int D, bool FP8>
+static hipError_t launch_rb(const ScoreArgs& a, hipStream_t s) {
+  const int groups = (a.nq + 15) / 16;
+  dim3 grid((unsigned)(groups * a.nsplit)), block(kThreads);
+  if (a.rows) {
+    hipLaunchKernelGGL((score_tile_kernel<RB, D, FP8, true>), grid, block, 0, s, a);
+  } else {
+    hipLaunchKernelGGL((score_tile_kernel<RB, D, FP8, false>), grid, block, 0, s, a);
+  }
+  return hipGetLastError();
+}
+
+hipError_t launch_score(const ScoreArgs& a, int d, bool fp8, hipStream_t s) {
+  if (a.nq <= 0) return hipSuccess;
+  const bool small = a.H <= 8;
+  if (fp8) {
+    if (d != 128) return hipErrorInvalidValue;
+    return small ? launch_rb<1, 128, true>(a, s) : launch_rb<8, 128, true>(a, s);
+  }
+  if (d == 64) return small ? launch_rb<1, 64, false>(a, s) : launch_rb<8, 64, false>(a, s);
+  if (d == 128) return small ? launch_rb<1, 128, false>(a, s) : launch_rb<8, 128, false>(a, s);
+  return hipErrorInvalidValue;
+}
+
+}  // namespace hk

@@ -1,0 +1,174 @@
+/*
+ * hytopk.h -- C ABI of the exact top-k indexer selection library for AMD
+ * Instinct MI355X (gfx950).
+ *
+ * Operation (HyScale pages):
+ *   * Learned sparse attention scores every earlier token of each query with
+ *     an indexer and keeps the k best; the conventional route writes the full
+ *     query x key score table to GPU memory and a second kernel reads it back
+ *     for top-k ("HyScale sparse-attention training -- Selection without a
+ *     score table", contest paragraph).
+ *   * HyTopK (also called FlashTopK) returns each query's exact top-k without
+ *     that table: a threshold taken from evenly spaced samples of the query's
+ *     own context, a fused score-and-compare pass that writes only passing keys
+ *     into a bounded candidate buffer, a check for overflow or fewer than k
+ *     candidates, recovery of the flagged queries, a full rescore when more
+ *     than 64 queries fail, ties at the k-th score resolved by a radix select
+ *     over positions, and a radix sort of the kept k (same page, HyTopK
+ *     paragraph; the paper's abstract).
+ *   * Selection replay keeps the k indices per query and, in recomputation,
+ *     rescores only those entries (same page, selection-replay paragraph).
+ *
+ * Indexer: I(t,s) = sum_h w[t,h] * ReLU(q[t,h] . k[s]), for key positions
+ * s = 0..t (a query sees itself and every earlier key).  Result order: score
+ * descending, then position ascending; at equal scores the lower position wins.
+ *
+ * Conventions for every entry point
+ *   * All array arguments are DEVICE pointers to row-major, contiguous data on
+ *     the current HIP device, except `stats`, which is a host pointer.
+ *   * q is [n][H][d], k is [L][d]: bf16, or OCP FP8 E4M3 bytes (dtype
+ *     HYTOPK_FP8_E4M3) with fp32 per-token dequantisation scales q_scale[n]
+ *     and k_scale[L] (> 0; NULL for bf16).  w is [n][H] fp32.  Query i sits at
+ *     position q_start + i and q_start + n <= L.
+ *   * Index outputs are [n][k] int32, score outputs [n][k] fp32.  When a
+ *     query's context ctx = q_start + i + 1 is shorter than k, the entries
+ *     beyond ctx hold index -1 and score -inf.
+ *   * `stream` is a hipStream_t (NULL = the legacy default stream).  Every
+ *     call is ordered on it.  hytopk_select synchronises that stream once (to
+ *     read the failure count); replay and baseline are fully asynchronous.
+ *   * Ownership: the caller allocates every buffer, including the workspace.
+ *     The library allocates no device memory.
+ *   * Errors: arguments are validated before any launch, so a negative return
+ *     means nothing was launched (HYTOPK_EHIP excepted: a HIP call failed
+ *     after launches may have started).  hytopk_last_error() gives text for
+ *     the calling thread's most recent failure.
+ *   * Supported in this version: 1 <= H <= 64 (heads beyond a multiple of 8
+ *     are zero-padded; H <= 8 uses a narrow tile); d in {64, 128} for bf16,
+ *     d = 128 for FP8 E4M3; 1 <= k <= 2048; L < 2^31; cap <= 16384 and
+ *     m_max <= 16384.  Other shapes return HYTOPK_EUNSUPPORTED.
+ */
+#ifndef HYTOPK_H_
+#define HYTOPK_H_
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  HYTOPK_OK = 0,
+  HYTOPK_EINVAL = -1,        /* bad argument: null pointer, bad size, q_start + n > L */
+  HYTOPK_EUNSUPPORTED = -2,  /* valid but not implemented (shape, dtype, k) */
+  HYTOPK_EWORKSPACE = -3,    /* workspace missing, too small or misaligned (256 B) */
+  HYTOPK_EHIP = -4           /* a HIP runtime call failed; see hytopk_last_error() */
+} hytopk_status;
+
+typedef enum { HYTOPK_BF16 = 0, HYTOPK_FP8_E4M3 = 1 } hytopk_dtype;
+
+/* Path overrides for testing; results are identical on every path. */
+typedef enum {
+  HYTOPK_PATH_AUTO = 0,     /* threshold + candidates, recovery or full rescore as the check decides */
+  HYTOPK_PATH_ROWS_ALL = 1  /* skip the threshold: score every row, then row top-k (the full rescore) */
+} hytopk_path;
+
+typedef struct {
+  int64_t L;        /* number of keys */
+  int64_t n;        /* number of queries */
+  int64_t q_start;  /* position of query 0; query i has position q_start + i */
+  int32_t H;        /* indexer heads */
+  int32_t d;        /* head dimension */
+  int32_t k;        /* keys kept per query */
+  int32_t dtype;    /* hytopk_dtype of q and k */
+} hytopk_problem;
+
+/* Sampled-threshold parameters.  Zero selects the default shown.
+ * Sample count M = min(max(m_min, L / m_div), m_max) and the threshold is the
+ * ceil(oversample * k * M_q / ctx)-th best of the M_q = min(M, ctx) samples at
+ * positions floor(j * ctx / M_q) (HyScale explainer, HyTopK and worked-example
+ * paragraphs).  cap is the candidate-buffer capacity per query; a query with
+ * more than cap or fewer than min(k, ctx) candidates is recovered; more than
+ * max_recover failures trigger the full rescore. */
+typedef struct {
+  int32_t m_min;        /* 4096 */
+  int32_t m_max;        /* 8192 */
+  int32_t m_div;        /* 128 */
+  int32_t oversample;   /* 3 */
+  int32_t cap;          /* 6 * k */
+  int32_t max_recover;  /* 64 */
+  int32_t force_path;   /* HYTOPK_PATH_AUTO */
+  int32_t rows_chunk;   /* rows rescored per pass in the full rescore: min(n, max(max_recover, 2^29 / L)) */
+} hytopk_params;
+
+/* What one hytopk_select call did (host struct, filled when non-NULL). */
+typedef struct {
+  int32_t n_overflow;    /* queries with more than cap candidates */
+  int32_t n_underk;      /* queries with fewer than min(k, ctx) candidates */
+  int32_t n_failed;      /* queries flagged by the check (either reason) */
+  int32_t full_rescore;  /* 1 when every query went through the row path */
+  int64_t cand_total;    /* candidates over all queries (including beyond cap) */
+  int32_t cand_max;      /* largest per-query candidate count */
+  int32_t path;          /* 0 candidates (+recovery), 1 full rescore (check), 2 forced rows */
+} hytopk_stats;
+
+/* Workspace bytes hytopk_select needs for this problem and parameters
+ * (0 on invalid input).  The workspace must be 256-byte aligned. */
+size_t hytopk_select_workspace(const hytopk_problem* p, const hytopk_params* prm);
+
+/* Workspace bytes of hytopk_baseline_select: the n x L fp32 score table. */
+size_t hytopk_baseline_workspace(const hytopk_problem* p);
+
+/* Exact top-k per query without a score table (HyTopK).
+ * out_idx [n][k] int32 receives positions; out_score [n][k] fp32 their scores
+ * (may be NULL).  prm may be NULL (all defaults); stats may be NULL. */
+int hytopk_select(const hytopk_problem* p, const hytopk_params* prm,
+                  const void* q, const float* q_scale, const void* k, const float* k_scale,
+                  const float* w, int32_t* out_idx, float* out_score,
+                  void* workspace, size_t workspace_bytes, void* stream, hytopk_stats* stats);
+
+/* Selection replay: out_score[i][j] = I(q_start + i, idx[i][j]) for the saved
+ * indices idx [n][k] int32 (HyScale explainer, selection-replay paragraph).
+ * An index outside [0, L) is padding and gives -inf (never dereferenced);
+ * indices in (q_start + i, L) are scored although they lie after the query
+ * (callers pass indices that selection returned).  The scores are
+ * bit-identical to those hytopk_select returns for the same entries. */
+int hytopk_replay(const hytopk_problem* p, const void* q, const float* q_scale,
+                  const void* k, const float* k_scale, const float* w, const int32_t* idx,
+                  float* out_score, void* stream);
+
+/* The conventional route: write the n x L fp32 score table into the
+ * workspace, then a row top-k kernel reads it back.  Same outputs as
+ * hytopk_select. */
+int hytopk_baseline_select(const hytopk_problem* p, const void* q, const float* q_scale,
+                           const void* k, const float* k_scale, const float* w,
+                           int32_t* out_idx, float* out_score,
+                           void* workspace, size_t workspace_bytes, void* stream);
+
+const char* hytopk_status_string(int status);
+const char* hytopk_last_error(void);  /* thread-local; "" when none */
+
+/* Kernel tracing.  While enabled, every launch the library makes is bracketed
+ * by a pair of hipEvents recorded on the caller's stream, and the elapsed time
+ * is accumulated per phase name ("sample_tau", "score_compact", "check",
+ * "cand_select", "score_rows", "row_topk", "replay").  Process-wide; not for
+ * use with concurrent calls on different streams. */
+typedef struct {
+  char name[32];
+  int32_t launches;
+  double total_ms;
+} hytopk_trace_entry;
+
+/* Enable (1) or disable (0) tracing; enabling clears the accumulators.
+ * Returns the previous state. */
+int hytopk_trace_enable(int on);
+
+/* Waits for the recorded events, then copies up to `max` accumulated entries
+ * (host array) and returns how many phases exist (negative on a HIP error). */
+int hytopk_trace_read(hytopk_trace_entry* out, int max);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* HYTOPK_H_ */

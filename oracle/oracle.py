@@ -85,6 +85,27 @@ def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     return np.where((c & 0x7F) == 0x7F, np.nan, out)
 
 
+_BF16_TABLE = None
+_E4M3_TABLE = None
+
+
+def _bf16_lookup(bits: np.ndarray) -> np.ndarray:
+    """decode_bf16 applied through a table of all 65,536 patterns (fast path
+    for large arrays; the table is decode_bf16 itself)."""
+    global _BF16_TABLE
+    if _BF16_TABLE is None:
+        _BF16_TABLE = decode_bf16(np.arange(1 << 16, dtype=np.uint16))
+    return _BF16_TABLE[np.asarray(bits, dtype=np.uint16)]
+
+
+def _e4m3_lookup(codes: np.ndarray) -> np.ndarray:
+    """decode_e4m3 applied through a table of all 256 codes."""
+    global _E4M3_TABLE
+    if _E4M3_TABLE is None:
+        _E4M3_TABLE = decode_e4m3(np.arange(256, dtype=np.uint8))
+    return _E4M3_TABLE[np.asarray(codes, dtype=np.uint8)]
+
+
 class Decoded:
     """Exact fp64 view of one problem.  Queries are decoded on demand (the
     1M-key shapes hold 8,192 x 64 x 128 query values)."""
@@ -94,9 +115,10 @@ class Decoded:
         self.L, self.n, self.H, self.d, self.k = inp.L, inp.n, inp.H, inp.d, inp.k
         self.q_start = inp.L - inp.n
         if inp.dtype == "bf16":
-            self.keys = decode_bf16(inp.k_)
+            self.keys = _bf16_lookup(inp.k_)
         elif inp.dtype == "fp8":
-            self.keys = decode_e4m3(inp.k_) * inp.k_scale.astype(np.float64)[:, None]
+            self.keys = _e4m3_lookup(inp.k_)
+            self.keys *= inp.k_scale.astype(np.float64)[:, None]
         else:
             raise ValueError(inp.dtype)
 
@@ -104,9 +126,9 @@ class Decoded:
         """(q[i] as [H][d] fp64, w[i] as [H] fp64)."""
         inp = self.inp
         if inp.dtype == "bf16":
-            q = decode_bf16(inp.q[i])
+            q = _bf16_lookup(inp.q[i])
         else:
-            q = decode_e4m3(inp.q[i]) * float(inp.q_scale[i])
+            q = _e4m3_lookup(inp.q[i]) * float(inp.q_scale[i])
         return q, inp.w[i].astype(np.float64)
 
     def position(self, i: int) -> int:

@@ -1,0 +1,95 @@
+"""The C ABI without a GPU: the library loads, exports every entry point that
+include/hytopk.h declares, and rejects bad arguments before touching HIP."""
+import ctypes
+import os
+import re
+import subprocess
+
+import pytest
+
+import exact_top_token_amd as hk
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "hytopk.h")
+
+
+def _declared():
+    src = open(HEADER).read()
+    return sorted(set(re.findall(r"\b(hytopk_[a-z_]+)\s*\(", src)))
+
+
+@pytest.fixture(scope="module")
+def lib():
+    if not os.path.exists(hk.library_path()):
+        pytest.fail("libhytopk.so is not built: run `python -m exact_top_token_amd.build`")
+    return hk.load_library()
+
+
+def test_header_declares_the_binding_exports():
+    assert _declared() == sorted(hk.EXPORTS)
+
+
+def test_library_exports_every_declared_symbol(lib):
+    out = subprocess.run(["nm", "-D", "--defined-only", hk.library_path()],
+                         capture_output=True, text=True, check=True).stdout
+    syms = {line.split()[-1] for line in out.splitlines() if line.strip()}
+    for name in _declared():
+        assert name in syms, name
+        assert getattr(lib, name) is not None
+
+
+def _prob(**kw):
+    base = dict(L=1 << 20, n=8192, q_start=(1 << 20) - 8192, H=64, d=128, k=2048, dtype=hk.BF16)
+    base.update(kw)
+    return hk.Problem(**base)
+
+
+def test_workspace_sizes_match_the_worked_example(lib):
+    p = _prob()
+    # the conventional table: 8192 x 1,048,576 fp32 = 32 GiB per layer
+    assert lib.hytopk_baseline_workspace(ctypes.byref(p)) == 32 << 30
+    ws = lib.hytopk_select_workspace(ctypes.byref(p), None)
+    # candidates at cap = 6k: 8192 x 12288 x 8 bytes, plus the recovery rows
+    assert ws >= 8192 * 12288 * 8
+    assert ws < 4 << 30
+    assert ws % 256 == 0
+
+
+@pytest.mark.parametrize("kw,code", [
+    (dict(n=0), -1), (dict(q_start=(1 << 20) - 8191), -1), (dict(k=0), -1),
+    (dict(k=4097), -2), (dict(H=65), -2), (dict(d=96), -2), (dict(dtype=1, d=64), -2),
+    (dict(dtype=7), -1), (dict(L=1 << 31, q_start=(1 << 31) - 8192), -2),
+])
+def test_invalid_problems_are_rejected_before_any_launch(lib, kw, code):
+    p = _prob(**kw)
+    assert lib.hytopk_select_workspace(ctypes.byref(p), None) == 0
+    rc = lib.hytopk_select(ctypes.byref(p), None, *([None] * 8), 0, None, None)
+    assert rc == code
+    assert lib.hytopk_last_error().decode()
+    rc = lib.hytopk_replay(ctypes.byref(p), *([None] * 8))
+    assert rc == code
+
+
+def test_null_pointers_and_workspace_errors(lib):
+    p = _prob()
+    fake = ctypes.c_void_p(0x1000)
+    assert lib.hytopk_select(ctypes.byref(p), None, None, None, fake, None, fake, fake, None,
+                             fake, 1 << 40, None, None) == -1
+    # workspace too small / misaligned -> -3, checked before any HIP call
+    assert lib.hytopk_select(ctypes.byref(p), None, fake, None, fake, None, fake, fake, None,
+                             fake, 16, None, None) == -3
+    assert lib.hytopk_select(ctypes.byref(p), None, fake, None, fake, None, fake, fake, None,
+                             ctypes.c_void_p(0x1001), 1 << 40, None, None) == -3
+    assert lib.hytopk_baseline_select(ctypes.byref(p), fake, None, fake, None, fake, fake, None,
+                                      fake, 1 << 20, None) == -3
+    # fp8 without scales -> -1
+    p8 = _prob(dtype=hk.FP8_E4M3)
+    assert lib.hytopk_replay(ctypes.byref(p8), fake, None, fake, None, fake, fake, fake, None) == -1
+    assert lib.hytopk_status_string(-3).decode() == "bad workspace"
+
+
+def test_bad_params_are_rejected(lib):
+    p = _prob()
+    for kw in (dict(cap=20000), dict(m_max=1 << 15), dict(force_path=5), dict(oversample=-1)):
+        prm = hk.Params(**kw)
+        assert lib.hytopk_select_workspace(ctypes.byref(p), ctypes.byref(prm)) == 0

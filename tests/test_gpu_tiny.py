@@ -1,0 +1,153 @@
+"""GPU parity on integer-valued inputs, where every fp32 score is exact, so the
+HIP path must equal the fp64 oracle bit for bit: the Tiny workload (L = 4,096,
+n = 256, H = 4, d = 64, k = 256, many ties), ragged shapes, every selection
+path (candidates, recovery, full rescore, forced rows, the baseline), replay,
+reproducibility and the threshold statistics."""
+import numpy as np
+import pytest
+import torch
+
+import datagen
+import oracle
+from gpu_util import assert_exact, oracle_rows, say, to_device
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.fixture(scope="module")
+def hk():
+    import exact_top_token_amd as m
+    m.load_library()
+    return m
+
+
+@pytest.fixture(scope="module")
+def tiny():
+    inp = datagen.make("tiny")
+    rows = oracle_rows(inp, range(inp.n))
+    ref = [oracle.exact_topk(r, inp.k) for r in rows]
+    return dict(inp=inp, dev=to_device(inp), rows=rows,
+                idx=np.stack([r[0] for r in ref]), val=np.stack([r[1] for r in ref]))
+
+
+def _np(t):
+    return t.cpu().numpy()
+
+
+def test_tiny_select_bit_exact(hk, tiny):
+    say("tiny: hytopk_select, L=4096 n=256 H=4 d=64 k=256")
+    d, inp = tiny["dev"], tiny["inp"]
+    idx, sc, st = hk.select(d["q"], d["k"], d["w"], inp.k, with_stats=True)
+    torch.cuda.synchronize()
+    assert_exact(inp, range(inp.n), _np(idx), _np(sc), tiny["idx"], tiny["val"])
+    assert st["path"] == 0 and st["n_failed"] == 0
+
+
+def test_tiny_stats_equal_threshold_prediction(hk, tiny):
+    """Integer scores: the GPU's thresholds and candidate counts must equal the
+    oracle's threshold model exactly."""
+    say("tiny: stats vs oracle.predict_paths")
+    d, inp = tiny["dev"], tiny["inp"]
+    _, _, st = hk.select(d["q"], d["k"], d["w"], inp.k, with_stats=True)
+    pred = oracle.predict_paths(tiny["rows"], inp.k, inp.L, cap=6 * inp.k)
+    assert st["cand_total"] == sum(p["cnt"] for p in pred["per_query"])
+    assert st["cand_max"] == max(p["cnt"] for p in pred["per_query"])
+    assert st["n_failed"] == pred["n_failed"]
+
+
+def test_tiny_replay_and_baseline_bit_exact(hk, tiny):
+    say("tiny: hytopk_replay + hytopk_baseline_select")
+    d, inp = tiny["dev"], tiny["inp"]
+    idx, sc = hk.select(d["q"], d["k"], d["w"], inp.k)
+    rep = hk.replay(d["q"], d["k"], d["w"], idx)
+    bidx, bsc = hk.baseline_select(d["q"], d["k"], d["w"], inp.k)
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(rep), _np(sc))
+    assert_exact(inp, range(inp.n), _np(bidx), _np(bsc), tiny["idx"], tiny["val"])
+    ref_rep = oracle.replay(inp, tiny["idx"])
+    assert np.array_equal(_np(rep).astype(np.float64), ref_rep)
+
+
+def test_tiny_every_path_is_identical(hk, tiny):
+    """Forced rows, forced overflow (full rescore) and a cap that sends a few
+    queries to recovery all return the same bits as the candidate path."""
+    d, inp = tiny["dev"], tiny["inp"]
+    base = [_np(t) for t in hk.select(d["q"], d["k"], d["w"], inp.k)]
+    cnts = np.array([p["cnt"] for p in oracle.predict_paths(tiny["rows"], inp.k, inp.L,
+                                                             cap=6 * inp.k)["per_query"]])
+    cap_few = int(np.sort(cnts)[-10])  # the 9 queries above it overflow
+    cases = [("rows_all", dict(force_path=hk.PATH_ROWS_ALL), 2, None),
+             ("overflow_all", dict(cap=inp.k + 1), 1, inp.n),
+             ("recovery", dict(cap=cap_few), 0, int(np.count_nonzero(cnts > cap_few))),
+             ("recovery_chunks", dict(cap=cap_few, rows_chunk=2, max_recover=64), 0, None),
+             ("full_rescore_chunks", dict(cap=inp.k + 1, rows_chunk=50), 1, inp.n)]
+    for name, prm, path, nfail in cases:
+        say(f"tiny: path {name} params {prm}")
+        idx, sc, st = hk.select(d["q"], d["k"], d["w"], inp.k, params=prm, with_stats=True)
+        torch.cuda.synchronize()
+        assert st["path"] == path, (name, st)
+        if nfail is not None:
+            assert st["n_failed"] == nfail, (name, st)
+        assert np.array_equal(_np(idx), base[0]), name
+        assert np.array_equal(_np(sc), base[1]), name
+
+
+def test_tiny_reproducible(hk, tiny):
+    say("tiny: three identical calls")
+    d, inp = tiny["dev"], tiny["inp"]
+    runs = [[_np(t) for t in hk.select(d["q"], d["k"], d["w"], inp.k)] for _ in range(3)]
+    for r in runs[1:]:
+        assert np.array_equal(r[0], runs[0][0]) and np.array_equal(r[1].view(np.uint32),
+                                                                   runs[0][1].view(np.uint32))
+
+
+@pytest.mark.parametrize("L,n,H,d,k,seed", [
+    (300, 300, 64, 128, 64, 5),     # q_start = 0: the first 63 queries have ctx < k
+    (1000, 37, 64, 128, 100, 6),    # ragged query group and key tile
+    (777, 77, 4, 64, 700, 7),       # k close to ctx, small heads
+    (5000, 130, 8, 128, 1, 8),      # k = 1
+    (4100, 33, 64, 64, 2048, 9),    # k = 2048 at H = 64, d = 64
+])
+def test_ragged_shapes_bit_exact(hk, L, n, H, d, k, seed):
+    say(f"ragged: L={L} n={n} H={H} d={d} k={k} seed={seed}")
+    inp = datagen.make_custom("ragged", L, n, H, d, k, dist="int", seed=seed)
+    dv = to_device(inp)
+    rows = oracle_rows(inp, range(n))
+    ref = [oracle.exact_topk(r, k) for r in rows]
+    ridx, rval = np.stack([r[0] for r in ref]), np.stack([r[1] for r in ref])
+    idx, sc = hk.select(dv["q"], dv["k"], dv["w"], k)
+    bidx, bsc = hk.baseline_select(dv["q"], dv["k"], dv["w"], k)
+    rep = hk.replay(dv["q"], dv["k"], dv["w"], idx)
+    torch.cuda.synchronize()
+    assert_exact(inp, range(n), _np(idx), _np(sc), ridx, rval)
+    assert_exact(inp, range(n), _np(bidx), _np(bsc), ridx, rval)
+    ok = ridx >= 0
+    assert np.array_equal(_np(rep)[ok], _np(sc)[ok])
+    assert np.all(np.isneginf(_np(rep)[~ok]))
+
+
+def test_explicit_q_start(hk):
+    """Queries need not sit at the end: q_start + n < L."""
+    say("q_start: L=2000 n=40 q_start=900")
+    inp = datagen.make_custom("qs", 2000, 40, 8, 64, 50, dist="int", seed=3)
+    dv = to_device(inp)
+    qs = 900
+    dec = oracle.Decoded(inp)
+    dec.q_start = qs
+    ref = [oracle.exact_topk(oracle.score_row(dec, i), inp.k) for i in range(inp.n)]
+    idx, sc = hk.select(dv["q"], dv["k"], dv["w"], inp.k, q_start=qs)
+    torch.cuda.synchronize()
+    assert_exact(inp, range(inp.n), _np(idx), _np(sc), np.stack([r[0] for r in ref]),
+                 np.stack([r[1] for r in ref]))
+
+
+def test_api_errors_do_not_launch(hk, tiny):
+    say("api errors")
+    d, inp = tiny["dev"], tiny["inp"]
+    with pytest.raises(hk.HytopkError) as e:
+        hk.select(d["q"], d["k"], d["w"], 5000)
+    assert e.value.status == -2
+    ws = torch.empty(16, dtype=torch.uint8, device="cuda")
+    with pytest.raises(hk.HytopkError) as e:
+        hk.baseline_select(d["q"], d["k"], d["w"], inp.k, workspace=ws[1:])
+    assert e.value.status == -3
