@@ -20,20 +20,34 @@
 
 namespace hk {
 
-constexpr int kTK = 64;          // keys per LDS tile
+constexpr int kTK = 64;          // keys per LDS stage
 constexpr int kThreads = 512;    // 8 waves = 8 query pairs
 constexpr int kSB = 128;         // staged candidates per query before a flush
 
+#define HK_LDS(x) ((__attribute__((address_space(3))) void*)(x))
+// s_waitcnt that only bounds the vector-memory counter (gfx9 encoding:
+// vmcnt[3:0] | expcnt[6:4] | lgkmcnt[11:8] | vmcnt[15:14]).
+#define HK_WAIT_VM(n) __builtin_amdgcn_s_waitcnt(((n) & 0xF) | (((n) >> 4) << 14) | (7 << 4) | (0xF << 8))
+
+// Key tiles stream through four LDS stages filled by direct-to-LDS loads
+// (global_load_lds_dwordx4), three tiles ahead of the one being scored, with
+// one workgroup barrier per tile.  The stages are distinct LDS objects so the
+// compiler can tell the loads into one stage from reads of another.
 template <int RB, int D, bool FP8, bool ROWS>
 __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
   using T = PairTile<RB, D, FP8>;
   using Frag = typename T::Frag;
-  constexpr int RBYTES = T::RBYTES, NCH = T::NCH, KS = T::KS, FB = T::FB;
+  constexpr int RBYTES = T::RBYTES, NCH = T::NCH, KS = T::KS;
   constexpr int TILE_BYTES = kTK * RBYTES;
-  constexpr int PER = kTK * NCH / kThreads;  // 16-byte chunks each thread stages per tile
-  static_assert((kTK * NCH) % kThreads == 0, "tile must split evenly over the workgroup");
+  constexpr int OPS = TILE_BYTES / (kThreads * 16);  // 16-byte DMA loads per lane per tile
+  constexpr int KPB = 1024 / RBYTES;                  // keys per 1 KB DMA block
+  constexpr int NCB = kTK / 16;                       // 16-key column blocks per tile
+  static_assert(TILE_BYTES % (kThreads * 16) == 0, "tile must split evenly over the workgroup");
 
-  __shared__ __attribute__((aligned(16))) uint8_t tile[2][TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t t0[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t t1[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t t2[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t t3[TILE_BYTES];
   __shared__ uint2 stage[ROWS ? 1 : 8][2][kSB];
   __shared__ int s_maxt[8];
 
@@ -59,6 +73,28 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
   const int ke = min(kb + a.split_len, maxt + 1);
   if (kb >= ke) return;  // uniform over the workgroup
   const int ntiles = (ke - kb + kTK - 1) / kTK;
+
+  // DMA layout: load p of wave w fills 1 KB block p * 8 + w of a stage; its
+  // lane j lands on key kk = block * KPB + j / NCH, 16-byte slot j % NCH,
+  // and fetches chunk (slot ^ (kk % NCH)) of that key: the swizzle the B
+  // fragment reads undo.  kk % NCH does not depend on p.
+  const int dma_kk = wave * KPB + lane / NCH;
+  const int dma_c = ((lane % NCH) ^ (dma_kk & (NCH - 1))) * 16;
+  const int full_tiles = (a.L - kb) / kTK;  // tiles that lie entirely below L
+  auto issue = [&](int tile, uint8_t* buf) {
+    const int k0 = kb + tile * kTK;
+    const uint8_t* base = a.k + (int64_t)k0 * RBYTES;
+#pragma unroll
+    for (int p = 0; p < OPS; ++p) {
+      const int kk = dma_kk + p * 8 * KPB;
+      int off = kk * RBYTES + dma_c;
+      if (tile >= full_tiles) off = (min(k0 + kk, a.L - 1) - k0) * RBYTES + dma_c;  // never past L
+      __builtin_amdgcn_global_load_lds(base + off, HK_LDS(buf + (p * 8 + wave) * 1024), 16, 0, 0);
+    }
+  };
+  issue(0, t0);
+  if (1 < ntiles) issue(1, t1);
+  if (2 < ntiles) issue(2, t2);
 
   T qt;
   qt.load(a.q, a.w, a.q_scale, a.H, qa, qb);
@@ -86,44 +122,16 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
       const int p = base + j;
       if (p < a.cap) dst[p] = stage[ROWS ? 0 : wave][which][j];
     }
+    HK_WAIT_VM(0);  // leave only stage loads in flight, so the per-tile counts stay exact
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
     __builtin_amdgcn_wave_barrier();
   };
 
-  u32x4 pre[PER];
-  auto gload = [&](int k0) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int idx = tid + p * kThreads;
-      const int kk = idx / NCH, c = idx % NCH;
-      const int gk = k0 + kk;
-      if (gk < a.L) {
-        pre[p] = *reinterpret_cast<const u32x4*>(a.k + (int64_t)gk * RBYTES + c * 16);
-      } else {
-        pre[p] = u32x4{0u, 0u, 0u, 0u};
-      }
-    }
-  };
-  auto lstore = [&](int buf) {
-#pragma unroll
-    for (int p = 0; p < PER; ++p) {
-      const int idx = tid + p * kThreads;
-      const int kk = idx / NCH, c = idx % NCH;
-      *reinterpret_cast<u32x4*>(&tile[buf][kk * RBYTES + ((c ^ (kk & (NCH - 1))) * 16)]) = pre[p];
-    }
-  };
-
-  gload(kb);
-  lstore(0);
-  __syncthreads();
-
-  for (int it = 0; it < ntiles; ++it) {
+  auto compute = [&](int it, const uint8_t* tb, const float (&ksc)[NCB]) {
     const int k0 = kb + it * kTK;
-    const int buf = it & 1;
-    if (it + 1 < ntiles) gload(k0 + kTK);
-    const uint8_t* tb = tile[buf];
+    float sc[NCB];
 #pragma unroll
-    for (int cb = 0; cb < kTK / 16; ++cb) {
+    for (int cb = 0; cb < NCB; ++cb) {
       const int kt = cb * 16 + (lane & 15);
       Frag b[KS];
 #pragma unroll
@@ -136,36 +144,82 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         } else {
           const int c = 4 * ks + g;
-          b[ks] = *reinterpret_cast<const bf16x8*>(tb + kt * RBYTES + ((c ^ (kt & (NCH - 1))) * 16));
+          b[ks] = *reinterpret_cast<const Frag*>(tb + kt * RBYTES + ((c ^ (kt & (NCH - 1))) * 16));
         }
       }
-      const int key = k0 + kt;
       float s = qt.score(b);
-      if constexpr (FP8) s *= (key < a.L) ? a.k_scale[key] : 0.0f;
-      const bool inrange = owner && key < lim;
-      if constexpr (ROWS) {
-        if (inrange) a.rows[(int64_t)es * a.row_stride + key] = s;
-      } else {
-        const bool pass = inrange && s >= tau;
-        const uint64_t m = __ballot(pass);
-        if (m) {
-          const uint32_t mA = (uint32_t)(m & 0xFFFFull);
-          const uint32_t mB = (uint32_t)((m >> 32) & 0xFFFFull);
-          if (pass) {
-            const uint32_t mm = sel ? mB : mA;
-            const int rank = __popc(mm & ((1u << (lane & 15)) - 1u));
-            const int slot = (sel ? cntB : cntA) + rank;
-            stage[wave][sel][slot] = make_uint2((uint32_t)key, __float_as_uint(s));
+      if constexpr (FP8) s *= ksc[cb];
+      sc[cb] = s;
+    }
+    if constexpr (ROWS) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int key = k0 + cb * 16 + (lane & 15);
+        if (owner && key < lim) a.rows[(int64_t)es * a.row_stride + key] = sc[cb];
+      }
+    } else {
+      // One uniform branch per tile: the candidate path runs only when some
+      // key of the tile passes (about one tile in three at 1M keys).
+      bool any = false;
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int key = k0 + cb * 16 + (lane & 15);
+        any |= owner && key < lim && sc[cb] >= tau;
+      }
+      if (__ballot(any)) {
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const int key = k0 + cb * 16 + (lane & 15);
+          const bool pass = owner && key < lim && sc[cb] >= tau;
+          const uint64_t m = __ballot(pass);
+          if (m) {
+            const uint32_t mA = (uint32_t)(m & 0xFFFFull);
+            const uint32_t mB = (uint32_t)((m >> 32) & 0xFFFFull);
+            if (pass) {
+              const uint32_t mm = sel ? mB : mA;
+              const int rank = __popc(mm & ((1u << (lane & 15)) - 1u));
+              const int slot = (sel ? cntB : cntA) + rank;
+              stage[wave][sel][slot] = make_uint2((uint32_t)key, __float_as_uint(sc[cb]));
+            }
+            cntA += __popc(mA);
+            cntB += __popc(mB);
+            if (cntA > kSB - 16) { flush(0, cntA); cntA = 0; }
+            if (cntB > kSB - 16) { flush(1, cntB); cntB = 0; }
           }
-          cntA += __popc(mA);
-          cntB += __popc(mB);
-          if (cntA > kSB - 16) { flush(0, cntA); cntA = 0; }
-          if (cntB > kSB - 16) { flush(1, cntB); cntB = 0; }
         }
       }
     }
-    if (it + 1 < ntiles) lstore(buf ^ 1);
-    __syncthreads();
+  };
+
+  // Per tile: wait for this wave's loads of tile `it`, barrier (every wave's
+  // loads landed; every wave finished tile it-1), refill tile it-1's stage
+  // with tile it+3, score tile it.  FP8 key scales are read before the refill
+  // so that waiting for them never waits for the refill.
+  auto step = [&](int it, const uint8_t* cur, uint8_t* refill) {
+    float ksc[NCB];
+    if constexpr (FP8) {
+#pragma unroll
+      for (int cb = 0; cb < NCB; ++cb) {
+        const int key = kb + it * kTK + cb * 16 + (lane & 15);
+        ksc[cb] = a.k_scale[min(key, a.L - 1)];
+      }
+    }
+    if (it + 2 < ntiles) {
+      HK_WAIT_VM(2 * OPS + (FP8 ? NCB : 0));
+    } else if (it + 1 < ntiles) {
+      HK_WAIT_VM(OPS + (FP8 ? NCB : 0));
+    } else {
+      HK_WAIT_VM(FP8 ? NCB : 0);
+    }
+    __builtin_amdgcn_s_barrier();
+    if (it + 3 < ntiles) issue(it + 3, refill);
+    compute(it, cur, ksc);
+  };
+  for (int it = 0; it < ntiles; it += 4) {
+    step(it, t0, t3);
+    if (it + 1 < ntiles) step(it + 1, t1, t0);
+    if (it + 2 < ntiles) step(it + 2, t2, t1);
+    if (it + 3 < ntiles) step(it + 3, t3, t2);
   }
   if constexpr (!ROWS) {
     if (cntA > 0) flush(0, cntA);
