@@ -94,6 +94,9 @@ def main() -> int:
     ap.add_argument("--no-baseline", action="store_true", help="skip the score-table baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
+                    help="only run one plain device-to-device copy of BYTES bytes (calibrates "
+                         "the HBM byte counters of a profiler run) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
         print("bench.py measures one GPU: the selection path has no multi-GPU mode in this "
@@ -102,6 +105,16 @@ def main() -> int:
 
     import numpy as np
     import torch
+
+    if args.copy_probe:
+        torch.cuda.set_device(0)
+        x = torch.ones(args.copy_probe // 4, dtype=torch.float32, device="cuda:0")
+        y = torch.empty_like(x)
+        torch.cuda.synchronize()
+        y.copy_(x)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": args.copy_probe}), flush=True)
+        return 0
 
     import datagen
     import exact_top_token_amd as hk

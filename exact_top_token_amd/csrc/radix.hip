@@ -24,7 +24,7 @@ namespace hk {
 
 constexpr int kSelThreads = 512;
 constexpr int kSelWaves = kSelThreads / kWave;
-constexpr int kMaxRounds = 8;  // k <= 4096 = kMaxRounds * kSelThreads
+constexpr int kMaxRounds = 4;  // k <= 2048 = kMaxRounds * kSelThreads
 
 // ----------------------------------------------------------------- helpers
 
@@ -54,7 +54,7 @@ __device__ void block_scan_excl(int* v, int m, int* wsum) {
 // Stable LSD radix sort, ascending by key bits [lo, hi) in 4-bit digits, of
 // the N (key, val) pairs in (k0, v0); (k1, v1) is scratch of the same size.
 // Returns true when the result ended in (k1, v1).
-__device__ bool block_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int N,
+__device__ __forceinline__ bool block_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int N,
                                  int lo, int hi, SortScratch& ss) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int rounds = (N + kSelThreads - 1) / kSelThreads;
@@ -64,15 +64,15 @@ __device__ bool block_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint3
     int myd[kMaxRounds], myrank[kMaxRounds];
 #pragma unroll
     for (int j = 0; j < kMaxRounds; ++j) {
-      if (j >= rounds) break;
       const int i = j * kSelThreads + tid;
-      const bool ok = i < N;
+      const bool ok = j < rounds && i < N;
       const int d = ok ? (int)((k0[i] >> sh) & 15u) : 16;
       int rank = 0;
+#pragma unroll
       for (int b = 0; b < 16; ++b) {
         const uint64_t mb = __ballot(d == b);
         if (d == b) rank = __popcll(mb & lt);
-        if (lane == 0) ss.cnt[b][j][wave] = __popcll(mb);
+        if (lane == 0 && j < rounds) ss.cnt[b][j][wave] = __popcll(mb);
       }
       myd[j] = d;
       myrank[j] = rank;
@@ -99,9 +99,8 @@ __device__ bool block_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint3
     block_scan_excl(&ss.cnt[0][0][0], 16 * kMaxRounds * kSelWaves, ss.wsum);
 #pragma unroll
     for (int j = 0; j < kMaxRounds; ++j) {
-      if (j >= rounds) break;
       const int i = j * kSelThreads + tid;
-      if (i < N) {
+      if (j < rounds && i < N) {
         const int dst = ss.cnt[myd[j]][j][wave] + myrank[j];
         k1[dst] = k0[i];
         v1[dst] = v0[i];
@@ -169,7 +168,7 @@ hipError_t launch_check(const int* cnt, int n, int q_start, int topk, int cap, D
 // Sort the `need` selected (key, pos) pairs by (score desc, pos asc) and write
 // the output row; entries need..topk-1 are padding.  pos_sorted: the pairs
 // are already in ascending position order, so a stable sort by score suffices.
-__device__ void sort_and_emit(uint32_t* sk, uint32_t* sp, uint32_t* tk, uint32_t* tp, int need,
+__device__ __forceinline__ void sort_and_emit(uint32_t* sk, uint32_t* sp, uint32_t* tk, uint32_t* tp, int need,
                               int topk, int L, bool pos_sorted, int* out_idx, float* out_score,
                               SortScratch& ss) {
   const int tid = threadIdx.x;
