@@ -29,7 +29,7 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}   # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "HyTopK select ms + TFLOP/s (%MFMA peak) at L=1M,n=8192,k=2048; replay ms"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic.json")
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_score_tile_glm1m_bf16.txt")
 KERNEL_SOURCES = ["exact_top_token_amd/csrc/score.hip", "exact_top_token_amd/csrc/tile.h",
                   "exact_top_token_amd/csrc/common.h"]
 
