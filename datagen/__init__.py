@@ -47,6 +47,7 @@ CONFIGS = {
     "glm1m": dict(L=1048576, n=8192, H=64, d=128, k=2048, dtype="bf16", dist="normal", seed=1003),
     "glm1m_fp8": dict(L=1048576, n=8192, H=64, d=128, k=2048, dtype="fp8", dist="normal", seed=1003),
 }
+STRESS_NAMES = ("stress_a", "stress_b")   # built by datagen.stress
 
 
 @dataclasses.dataclass

@@ -42,10 +42,12 @@ class Stats(ctypes.Structure):
     _fields_ = [("n_overflow", ctypes.c_int32), ("n_underk", ctypes.c_int32),
                 ("n_failed", ctypes.c_int32), ("full_rescore", ctypes.c_int32),
                 ("cand_total", ctypes.c_int64), ("cand_max", ctypes.c_int32),
-                ("path", ctypes.c_int32)]
+                ("path", ctypes.c_int32), ("failed_queries", ctypes.POINTER(ctypes.c_int32)),
+                ("failed_capacity", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
     def as_dict(self) -> dict:
-        return {f: getattr(self, f) for f, _ in self._fields_}
+        return {f: getattr(self, f) for f, _ in self._fields_
+                if f not in ("failed_queries", "failed_capacity", "reserved")}
 
 
 class TraceEntry(ctypes.Structure):
@@ -196,10 +198,19 @@ def select(q, k, w, topk: int, *, q_scale=None, k_scale=None, q_start=None, para
     else:
         idx, score = out
     st = Stats()
+    failed_buf = None
+    if with_stats:
+        failed_buf = (ctypes.c_int32 * int(prob.n))()
+        st.failed_queries = ctypes.cast(failed_buf, ctypes.POINTER(ctypes.c_int32))
+        st.failed_capacity = int(prob.n)
     _check(lib.hytopk_select(ctypes.byref(prob), ctypes.byref(prm) if prm else None, _ptr(q),
                              _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), _ptr(idx), _ptr(score),
                              _ptr(workspace), workspace.numel(), _stream(q), ctypes.byref(st)))
-    return (idx, score, st.as_dict()) if with_stats else (idx, score)
+    if not with_stats:
+        return idx, score
+    d = st.as_dict()
+    d["failed"] = [failed_buf[i] for i in range(min(st.n_failed, int(prob.n)))]
+    return idx, score, d
 
 
 def replay(q, k, w, idx, *, q_scale=None, k_scale=None, q_start=None, out=None):

@@ -388,6 +388,14 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
       if (rc) return rc;
     }
   }
+  if (stats && stats->failed_queries && stats->failed_capacity > 0 && hs.n_failed > 0) {
+    const int m = std::min(hs.n_failed, stats->failed_capacity);
+    HK_HIP(hipMemcpyAsync(stats->failed_queries, failed, (size_t)m * sizeof(int32_t),
+                          hipMemcpyDeviceToHost, s),
+           "failed list copy");
+    HK_HIP(hipStreamSynchronize(s), "stream sync");
+    std::sort(stats->failed_queries, stats->failed_queries + m);
+  }
   if (stats) {
     stats->n_overflow = hs.n_overflow;
     stats->n_underk = hs.n_underk;

@@ -101,15 +101,21 @@ typedef struct {
   int32_t rows_chunk;   /* rows rescored per pass in the full rescore: min(n, max(max_recover, 2^29 / L)) */
 } hytopk_params;
 
-/* What one hytopk_select call did (host struct, filled when non-NULL). */
+/* What one hytopk_select call did (host struct, filled when non-NULL).
+ * failed_queries / failed_capacity are inputs: when failed_queries is a host
+ * array, it receives the indices of up to failed_capacity queries the check
+ * flagged, in ascending order (read during the call's one synchronisation). */
 typedef struct {
-  int32_t n_overflow;    /* queries with more than cap candidates */
-  int32_t n_underk;      /* queries with fewer than min(k, ctx) candidates */
-  int32_t n_failed;      /* queries flagged by the check (either reason) */
-  int32_t full_rescore;  /* 1 when every query went through the row path */
-  int64_t cand_total;    /* candidates over all queries (including beyond cap) */
-  int32_t cand_max;      /* largest per-query candidate count */
-  int32_t path;          /* 0 candidates (+recovery), 1 full rescore (check), 2 forced rows */
+  int32_t n_overflow;      /* queries with more than cap candidates */
+  int32_t n_underk;        /* queries with fewer than min(k, ctx) candidates */
+  int32_t n_failed;        /* queries flagged by the check (either reason) */
+  int32_t full_rescore;    /* 1 when every query went through the row path */
+  int64_t cand_total;      /* candidates over all queries (including beyond cap) */
+  int32_t cand_max;        /* largest per-query candidate count */
+  int32_t path;            /* 0 candidates (+recovery), 1 full rescore (check), 2 forced rows */
+  int32_t* failed_queries; /* in: optional host array for the flagged query indices */
+  int32_t failed_capacity; /* in: its length */
+  int32_t reserved;
 } hytopk_stats;
 
 /* Workspace bytes hytopk_select needs for this problem and parameters

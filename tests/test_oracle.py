@@ -316,3 +316,21 @@ def test_brute_force_signed_weights():
         S, keep = _brute_select(inp, i)
         assert list(idx[i, : len(keep)]) == keep
         assert [Fraction(v) for v in val[i, : len(keep)]] == [S[a] for a in keep]
+
+
+def test_stress_generator_failures_match_threshold_model():
+    """The planted groups of the recovery-stress workload fail the check with a
+    margin >= 1,024 under the oracle's threshold model; their neighbours and
+    ordinary queries do not."""
+    inp = datagen.make("stress_a")
+    dec = oracle.Decoded(inp)
+    over, under = inp.planted_over, inp.planted_under
+    qs = [int(over[0]), int(over[-1]), int(under[0]), int(under[-1]),
+          int(under[0]) - 1, int(under[-1]) + 1, 0, inp.n - 1]
+    rows = [oracle.score_row(dec, i) for i in qs]
+    pred = oracle.predict_paths(rows, inp.k, inp.L, cap=6 * inp.k)["per_query"]
+    assert pred[0]["overflow"] and pred[1]["overflow"]
+    assert pred[2]["underk"] and pred[3]["underk"]
+    assert min(-pred[0]["margin_cap"], -pred[1]["margin_cap"]) >= 1024
+    assert min(-pred[2]["margin_k"], -pred[3]["margin_k"]) >= 1024
+    assert not any(p["fail"] for p in pred[4:])
