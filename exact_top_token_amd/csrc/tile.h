@@ -16,10 +16,9 @@
 //     hold 32 heads of query A (heads 8rb + 4(g & 1) + i), lanes 32..63 the
 //     same heads of query B.
 // Epilogue: each lane sums w * max(acc, 0) over its 32 heads in a fixed order
-// (row block, then register), then adds its partner lane (lane ^ 16).  Every
-// kernel that produces a score uses exactly this code, so a (query, key)
-// score is bit-identical whichever kernel, tile position or query pairing
-// computed it.
+// (two partials, see epilogue()), then adds its partner lane (lane ^ 16).  A
+// (query, key) score is bit-identical whichever kernel, tile position or query
+// pairing computed it.
 #pragma once
 
 #include "common.h"
@@ -98,14 +97,27 @@ struct PairTile {
     return epilogue(acc);
   }
 
+  // Canonical head-sum order (every kernel that produces a score follows it):
+  // per lane, one partial over the even row blocks and one over the odd row
+  // blocks (row block ascending, register ascending), t = even + odd, then
+  // t + t(lane ^ 16).  A tile holding one query per MFMA (16 heads per row
+  // block) sees the same four partials in its four lane groups.
   __device__ __forceinline__ float epilogue(const f32x4 (&acc)[RB]) const {
-    float s = 0.0f;
+    float se = 0.0f, so = 0.0f;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s = __builtin_fmaf(__builtin_fmaxf(acc[rb][i], 0.0f), wf[rb][i], s);
+      for (int i = 0; i < 4; ++i) {
+        const float r = __builtin_fmaxf(acc[rb][i], 0.0f);
+        if (rb & 1) {
+          so = __builtin_fmaf(r, wf[rb][i], so);
+        } else {
+          se = __builtin_fmaf(r, wf[rb][i], se);
+        }
+      }
     }
-    return s + __shfl_xor(s, 16);
+    const float t = se + so;
+    return t + __shfl_xor(t, 16);
   }
 };
 
