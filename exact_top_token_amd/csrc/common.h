@@ -52,30 +52,34 @@ __device__ __forceinline__ int wave_prefix_excl(int x) {
 }
 
 // Shared scratch of the block radix select: 256 histogram bins, 4 wave
-// totals, and the chosen digit / remaining rank.
+// totals, and the chosen digit / remaining rank / multiplicity.
 struct RadixScratch {
   int hist[256];
   int wtot[4];
   uint32_t digit;
   int rank;
+  int mult;
 };
 
 // Block-wide radix select: the r-th largest (1-based, duplicates counted)
-// value of key(i) over the i in [0, m) with take(i).  MSB-first, 8-bit digits.
+// value of key(i) over the i in [0, m) with take(i).  Keys must lie below
+// 2^bits (bits <= 32); MSB-first passes of 8-bit digits cover only those bits.
 // Requires blockDim.x >= 256 and a multiple of 64; all threads must call it.
 // On return `rem` is the rank of the result among the entries equal to it
-// (1 <= rem <= multiplicity), i.e. how many equal entries complete the top r.
+// (1 <= rem <= mult), and `mult` how many taken entries equal it.
 template <typename KeyF, typename TakeF>
 __device__ uint32_t block_select_largest(int m, int r, KeyF key, TakeF take, RadixScratch& sc,
-                                          int& rem) {
+                                          int& rem, int& mult, int bits = 32) {
   const int tid = threadIdx.x, nt = blockDim.x;
   uint32_t prefix = 0u, pmask = 0u;
-  for (int shift = 24; shift >= 0; shift -= 8) {
+  const int npass = bits <= 0 ? 1 : (bits + 7) / 8;
+  for (int pass = npass - 1; pass >= 0; --pass) {
+    const int shift = 8 * pass;
     for (int b = tid; b < 256; b += nt) sc.hist[b] = 0;
     __syncthreads();
     for (int i = tid; i < m; i += nt) {
       if (!take(i)) continue;
-      uint32_t kk = key(i);
+      const uint32_t kk = key(i);
       if ((kk & pmask) == prefix) atomicAdd(&sc.hist[(kk >> shift) & 255u], 1);
     }
     __syncthreads();
@@ -92,6 +96,7 @@ __device__ uint32_t block_select_largest(int m, int r, KeyF key, TakeF take, Rad
       if (suf >= r && suf - h < r) {
         sc.digit = (uint32_t)tid;
         sc.rank = r - (suf - h);
+        sc.mult = h;
       }
     }
     __syncthreads();
@@ -101,7 +106,28 @@ __device__ uint32_t block_select_largest(int m, int r, KeyF key, TakeF take, Rad
     __syncthreads();
   }
   rem = r;
+  mult = sc.mult;
   return prefix;
+}
+
+// Number of bits needed for values in [0, x].
+__device__ __forceinline__ int bit_width(uint32_t x) { return x ? 32 - __clz(x) : 0; }
+
+// Block-wide min and max of one value per thread (all threads must call).
+__device__ __forceinline__ void block_minmax(uint32_t lo, uint32_t hi, uint32_t* red,
+                                             uint32_t& gmin, uint32_t& gmax) {
+  const int tid = threadIdx.x, nw = blockDim.x / kWave;
+#pragma unroll
+  for (int off = 32; off > 0; off >>= 1) {
+    lo = min(lo, (uint32_t)__shfl_xor((int)lo, off));
+    hi = max(hi, (uint32_t)__shfl_xor((int)hi, off));
+  }
+  if (lane_id() == 0) { red[tid >> 6] = lo; red[nw + (tid >> 6)] = hi; }
+  __syncthreads();
+  gmin = red[0];
+  gmax = red[nw];
+  for (int w = 1; w < nw; ++w) { gmin = min(gmin, red[w]); gmax = max(gmax, red[nw + w]); }
+  __syncthreads();
 }
 
 }  // namespace hk

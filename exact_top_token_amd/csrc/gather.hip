@@ -238,9 +238,9 @@ __global__ void __launch_bounds__(kSampleThreads) sample_tau_kernel(SampleArgs a
     if (lane < 16 && j < mq) S[j] = s;
   }
   __syncthreads();
-  int rem;
+  int rem, mult;
   const uint32_t v = block_select_largest(
-      mq, r, [&](int i) { return score_key(S[i]); }, [](int) { return true; }, sc, rem);
+      mq, r, [&](int i) { return score_key(S[i]); }, [](int) { return true; }, sc, rem, mult);
   if (tid == 0) a.tau[q] = key_score(v);
 }
 

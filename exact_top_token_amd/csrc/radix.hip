@@ -199,73 +199,127 @@ __device__ __forceinline__ void sort_and_emit(uint32_t* sk, uint32_t* sp, uint32
 struct CandShared {
   RadixScratch rs;
   SortScratch ss;
+  uint32_t red[2 * kSelWaves];
   int nsel;
+  int tie;
 };
 
 size_t cand_select_lds_bytes(int cap, int topk) {
-  // candidates (key + pos) followed by the selected pairs (key + pos)
-  return (size_t)cap * 8 + (size_t)topk * 8;
+  // candidate score keys (reused as the sort's scratch pairs), then the
+  // selected pairs (key + position)
+  return (size_t)(cap > 2 * topk ? cap : 2 * topk) * 4 + (size_t)topk * 8;
 }
 
+// One workgroup per query that passed the check.  Only the candidates' score
+// keys are staged in LDS (positions stay in the candidate buffer and are read
+// for the kept entries only), so two workgroups fit on a CU.  The scores of a
+// query's candidates span a narrow range, so the radix digits start at the
+// highest bit in which two candidate keys differ.
 __global__ void __launch_bounds__(kSelThreads) cand_select_kernel(const int* cnt, const uint2* cand,
                                                                   int q_start, int topk, int cap,
                                                                   int L, int* out_idx,
                                                                   float* out_score) {
   extern __shared__ uint32_t dyn[];
   __shared__ CandShared sh;
-  const int q = blockIdx.x, tid = threadIdx.x;
+  const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int c = cnt[q];
   const int ctx = q_start + q + 1;
   const int need = min(topk, ctx);
   if (c > cap || c < need) return;  // failed: recovered on the row path
-  uint32_t* ck = dyn;               // [cap] score keys
-  uint32_t* cp = dyn + cap;         // [cap] positions
-  uint32_t* sk = dyn + 2 * cap;     // [topk] selected keys
-  uint32_t* sp = sk + topk;         // [topk] selected positions
+  uint32_t* ck = dyn;               // [cap] candidate score keys (later: sort scratch)
+  uint32_t* sk = dyn + max(cap, 2 * topk);  // [topk] kept keys
+  uint32_t* sp = sk + topk;         // [topk] kept positions
   const uint2* src = cand + (int64_t)q * cap;
+  uint32_t lo = 0xFFFFFFFFu, hi = 0u;
   for (int i = tid; i < c; i += kSelThreads) {
-    const uint2 e = src[i];
-    cp[i] = e.x;
-    ck[i] = score_key(__uint_as_float(e.y));
+    const uint32_t kk = score_key(__uint_as_float(src[i].y));
+    ck[i] = kk;
+    lo = min(lo, kk);
+    hi = max(hi, kk);
   }
   if (tid == 0) sh.nsel = 0;
-  __syncthreads();
-  int rem;
-  const uint32_t v = block_select_largest(
-      c, need, [&](int i) { return ck[i]; }, [](int) { return true; }, sh.rs, rem);
-  // rem = how many entries equal to v belong to the top k: keep the rem
-  // lowest positions among them (position select: largest of ~pos).
+  uint32_t kmin, kmax;
+  block_minmax(lo, hi, sh.red, kmin, kmax);  // includes the barrier after the loads
+  // k-th largest key, as an offset above kmin
+  int rem, mult;
+  const uint32_t v = kmin + block_select_largest(
+      c, need, [&](int i) { return ck[i] - kmin; }, [](int) { return true; }, sh.rs, rem, mult,
+      bit_width(kmax - kmin));
+  // rem of the mult entries equal to v belong to the top k: keep the rem
+  // lowest positions among them (radix select over positions).
   uint32_t pmax = 0xFFFFFFFFu;
-  {
-    int mult = 0;
-    if (tid == 0) sh.rs.rank = 0;
-    __syncthreads();
-    int loc = 0;
-    for (int i = tid; i < c; i += kSelThreads) loc += (ck[i] == v);
-    if (loc) atomicAdd(&sh.rs.rank, loc);
-    __syncthreads();
-    mult = sh.rs.rank;
-    __syncthreads();
-    if (rem < mult) {
-      int rr;
-      pmax = ~block_select_largest(
-          c, rem, [&](int i) { return ~cp[i]; }, [&](int i) { return ck[i] == v; }, sh.rs, rr);
-    }
+  if (rem < mult) {
+    int rr, mm;
+    const uint32_t pb = (uint32_t)bit_width((uint32_t)(L - 1));
+    const uint32_t top = pb >= 32 ? 0xFFFFFFFFu : ((1u << pb) - 1u);
+    pmax = top - block_select_largest(
+        c, rem, [&](int i) { return top - src[i].x; }, [&](int i) { return ck[i] == v; }, sh.rs,
+        rr, mm, (int)pb);
   }
-  for (int i = tid; i < c; i += kSelThreads) {
-    const uint32_t kk = ck[i];
-    if (kk > v || (kk == v && cp[i] <= pmax)) {
-      const int slot = atomicAdd(&sh.nsel, 1);
+  // compaction: one slot reservation per wave and sweep
+  for (int i0 = 0; i0 < c; i0 += kSelThreads) {
+    const int i = i0 + tid;
+    bool keep = false;
+    uint32_t kk = 0u;
+    if (i < c) {
+      kk = ck[i];
+      keep = kk > v || (kk == v && (pmax == 0xFFFFFFFFu || src[i].x <= pmax));
+    }
+    const uint64_t m = __ballot(keep);
+    int base = 0;
+    if (lane == 0 && m) base = atomicAdd(&sh.nsel, __popcll(m));
+    base = __shfl(base, 0);
+    if (keep) {
+      const int slot = base + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
       if (slot < need) {  // exactly `need` entries qualify; the guard keeps LDS writes in bounds
         sk[slot] = kk;
-        sp[slot] = cp[i];
+        sp[slot] = src[i].x;
       }
     }
   }
   __syncthreads();
-  // The candidate area is free now: use it as the sort's scratch.
-  sort_and_emit(sk, sp, ck, cp, need, topk, L, false, out_idx + (int64_t)q * topk,
-                out_score ? out_score + (int64_t)q * topk : nullptr, sh.ss);
+  // Order by (score desc, position asc).  Sort on the offset of the key below
+  // the largest kept key (only its significant bits); positions are sorted
+  // first only if two kept entries have equal scores.
+  const uint32_t krange = kmax - v;
+  uint32_t* tk = ck;
+  uint32_t* tp = ck + topk;
+  for (int i = tid; i < need; i += kSelThreads) sk[i] = kmax - sk[i];
+  __syncthreads();
+  const int kbits = (bit_width(krange) + 3) & ~3;
+  const int pbits = (bit_width((uint32_t)(L - 1)) + 3) & ~3;
+  // One sort call site (stage 0: by key; on ties, stage 1: by position,
+  // stage 2: stable by key again), so the sort is inlined once.
+  uint32_t *rk = sk, *rp = sp, *xk = tk, *xp = tp;
+  for (int stage = 0;; ++stage) {
+    const bool byp = stage == 1;
+    const bool fl = block_sort_pairs(byp ? rp : rk, byp ? rk : rp, byp ? xp : xk, byp ? xk : xp,
+                                     need, 0, byp ? pbits : kbits, sh.ss);
+    if (fl) {
+      uint32_t* t = rk; rk = xk; xk = t;
+      t = rp; rp = xp; xp = t;
+    }
+    if (stage == 2) break;
+    if (stage == 0) {
+      if (tid == 0) sh.tie = 0;
+      __syncthreads();
+      for (int i = tid; i + 1 < need; i += kSelThreads)
+        if (rk[i] == rk[i + 1]) sh.tie = 1;
+      __syncthreads();
+      if (!sh.tie) break;  // uniform
+    }
+  }
+  int* oi = out_idx + (int64_t)q * topk;
+  float* os = out_score ? out_score + (int64_t)q * topk : nullptr;
+  for (int i = tid; i < topk; i += kSelThreads) {
+    if (i < need) {
+      oi[i] = (int)rp[i];
+      if (os) os[i] = key_score(kmax - rk[i]);
+    } else {
+      oi[i] = -1;
+      if (os) os[i] = -__builtin_inff();
+    }
+  }
 }
 
 hipError_t launch_cand_select(const int* cnt, const uint2* cand, int n, int q_start, int topk,
@@ -300,9 +354,10 @@ __global__ void __launch_bounds__(kSelThreads) row_topk_kernel(const float* rows
   const int ctx = q_start + q + 1;
   const int need = min(topk, ctx);
   const float* row = rows + (int64_t)e * row_stride;
-  int rem;
+  int rem, mult;
   const uint32_t v = block_select_largest(
-      ctx, need, [&](int i) { return score_key(row[i]); }, [](int) { return true; }, sh.rs, rem);
+      ctx, need, [&](int i) { return score_key(row[i]); }, [](int) { return true; }, sh.rs, rem,
+      mult);
   // Emit in position order: every key > v, and the first `rem` keys == v.
   const int seg = ((ctx + kSelWaves - 1) / kSelWaves + kWave - 1) / kWave * kWave;
   const int s0 = min(ctx, wave * seg), s1 = min(ctx, s0 + seg);
