@@ -33,7 +33,12 @@ score table]:
    form of that indexer: the head weight applies after the ReLU;
 3. order the context by score descending, then position ascending (lower
    position wins a tie) and keep the first min(k, ctx); pad with -1 / -inf;
-4. replay: I(t, idx) at the saved indices [Explainer, selection replay].
+4. replay: I(t, idx) at the saved indices [Explainer, selection replay];
+5. backward at the replayed entries: given an upstream gradient dI[t, j] for
+   the score at idx[t, j], the gradients of sum_{t,j} dI[t,j] * I(t, idx[t,j])
+   with respect to q, w and k.  The choice itself carries no gradient (top-k
+   is not differentiable) and the indexer's loss reads only the scores at the
+   selected entries, so nothing else enters [Explainer, key observation].
 
 The threshold model (``sample_count`` .. ``predict_paths``) is not part of the
 result.  It restates the HyTopK paragraph and the worked example so tests can
@@ -156,8 +161,7 @@ def score_row(dec: Decoded, i: int, chunk: int = 32768) -> np.ndarray:
 def score_pairs(dec: Decoded, i: int, keys: np.ndarray) -> np.ndarray:
     """I(t, s) for query i at the given key positions (any order)."""
     q, w = dec.query(i)
-    dots = q @ dec.keys[np.asarray(keys, dtype=np.int64)].T
-    return w @ np.maximum(dots, 0.0)
+    return indexer_pairs(q, w, dec.keys[np.asarray(keys, dtype=np.int64)])
 
 
 # ---------------------------------------------------------------------------
@@ -203,6 +207,103 @@ def replay(inp, idx: np.ndarray, queries=None) -> np.ndarray:
         if np.any(ok):
             out[r, ok] = score_pairs(dec, int(i), idx[r, ok])
     return out
+
+
+# ---------------------------------------------------------------------------
+# 3b. Backward at the replayed entries (plain chain rule, fp64).
+# ---------------------------------------------------------------------------
+
+
+def indexer_pairs(q: np.ndarray, w: np.ndarray, keys: np.ndarray) -> np.ndarray:
+    """I = sum_h w[h] * ReLU(q[h] . key) for one query (q [H][d], w [H]) and
+    the rows of ``keys`` ([m][d]); fp64 arrays in, fp64 [m] out."""
+    return w @ np.maximum(q @ keys.T, 0.0)
+
+
+def backward_query(q: np.ndarray, w: np.ndarray, keys: np.ndarray, g: np.ndarray,
+                   amb: float = 0.0) -> dict:
+    """Gradients of sum_j g[j] * I(q, w, keys[j]) for one query.
+
+    With c[h, j] = q[h] . keys[j] and the ReLU derivative taken as 1 where
+    c > 0 and 0 elsewhere (including c == 0):
+      dw[h]     = sum_j g[j] * max(c[h, j], 0)
+      dq[h, :]  = w[h] * sum_j g[j] * [c[h, j] > 0] * keys[j, :]
+      u[j, :]   = sum_h g[j] * w[h] * [c[h, j] > 0] * q[h, :]   (row j's share of dk)
+    Also returns the same sums over absolute values of every term (the scale
+    against which a rounding-error bound is stated) and, for ``amb`` > 0, the
+    absolute contribution of the terms whose ReLU decision is within
+    amb * sum_i |q[h, i] * keys[j, i]| of zero, where a lower-precision
+    evaluation of c may take the other branch.
+    """
+    c = q @ keys.T                                  # [H][m]
+    on = c > 0.0
+    dw = np.where(on, c, 0.0) @ g
+    G = np.where(on, g[None, :], 0.0)               # dI[j] * ReLU'(c)
+    dq = w[:, None] * (G @ keys)
+    u = (G * w[:, None]).T @ q
+    ag, aw, aq, ak = np.abs(g), np.abs(w), np.abs(q), np.abs(keys)
+    Ga = np.where(on, ag[None, :], 0.0)
+    out = dict(dw=dw, dq=dq, u=u,
+               dw_abs=np.where(on, c, 0.0) @ ag,
+               dq_abs=aw[:, None] * (Ga @ ak),
+               u_abs=(Ga * aw[:, None]).T @ aq)
+    if amb > 0.0:
+        near = np.abs(c) <= amb * (aq @ ak.T)
+        Gn = np.where(near, ag[None, :], 0.0)
+        out["dq_amb"] = aw[:, None] * (Gn @ ak)
+        out["u_amb"] = (Gn * aw[:, None]).T @ aq
+    return out
+
+
+def backward_core(query_fn, keys: np.ndarray, idx: np.ndarray, d_score: np.ndarray,
+                  amb: float = 0.0) -> dict:
+    """Backward over m queries: ``query_fn(r)`` gives query r's (q [H][d],
+    w [H]) in fp64, ``keys`` is [L][d] fp64, idx [m][k] key positions
+    (outside [0, L) = padding, no contribution), d_score [m][k] the upstream
+    gradient.  dk is the scatter-add of every entry's u row onto its key."""
+    idx = np.asarray(idx)
+    g_all = np.asarray(d_score, dtype=np.float64)
+    L, d = keys.shape
+    m = idx.shape[0]
+    res = None
+    for r in range(m):
+        q, w = query_fn(r)
+        if res is None:
+            H = q.shape[0]
+            res = {k: np.zeros((m, H, d)) for k in ("dq", "dq_abs")}
+            res.update({k: np.zeros((m, H)) for k in ("dw", "dw_abs")})
+            res.update({k: np.zeros((L, d)) for k in ("dk", "dk_abs")})
+            if amb > 0.0:
+                res["dq_amb"] = np.zeros((m, H, d))
+                res["dk_amb"] = np.zeros((L, d))
+        ok = (idx[r] >= 0) & (idx[r] < L)
+        if not np.any(ok):
+            continue
+        sel = idx[r, ok].astype(np.int64)
+        b = backward_query(q, w, keys[sel], g_all[r, ok], amb)
+        res["dq"][r], res["dq_abs"][r] = b["dq"], b["dq_abs"]
+        res["dw"][r], res["dw_abs"][r] = b["dw"], b["dw_abs"]
+        np.add.at(res["dk"], sel, b["u"])           # scatter-add by key position
+        np.add.at(res["dk_abs"], sel, b["u_abs"])
+        if amb > 0.0:
+            res["dq_amb"][r] = b["dq_amb"]
+            np.add.at(res["dk_amb"], sel, b["u_amb"])
+    return res
+
+
+def backward(inp, idx: np.ndarray, d_score: np.ndarray, queries=None, amb: float = 0.0) -> dict:
+    """Indexer backward at the replayed entries for the given query indices
+    (default: all n).  idx [m][k] holds key positions (negative = padding, no
+    contribution); d_score [m][k] the upstream gradient of each replayed
+    score.  FP8 inputs are differentiated with respect to their decoded
+    values (code times per-token scale).
+
+    Returns fp64 dq [m][H][d], dw [m][H], dk [L][d] (the queries' summed
+    contributions; keys no query selected get 0), their absolute-term scales
+    (*_abs) and, for amb > 0, the ambiguous-decision allowances (*_amb)."""
+    dec = Decoded(inp)
+    qs = np.arange(inp.n) if queries is None else np.asarray(queries, dtype=np.int64)
+    return backward_core(lambda r: dec.query(int(qs[r])), dec.keys, idx, d_score, amb)
 
 
 # ---------------------------------------------------------------------------
