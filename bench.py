@@ -58,6 +58,15 @@ def replay_bytes(n, H, d, k, fp8) -> int:
     return n * k * per_entry + n * per_query
 
 
+def backward_bytes(L, n, H, d, k) -> int:
+    """Algorithmic HBM bytes of the bf16 backward: per entry the key row, its
+    index and upstream gradient; per query q and w read, dq and dw written;
+    dk written once."""
+    per_entry = d * 2 + 4 + 4
+    per_query = H * (d * 2 + 4) + H * (d * 4 + 4)
+    return n * k * per_entry + n * per_query + L * d * 4
+
+
 def cpu_baseline(inp, seconds_target: float = 15.0) -> dict:
     """The oracle as it stands, on a bounded sample of the same workload."""
     import numpy as np
@@ -93,6 +102,8 @@ def main() -> int:
     ap.add_argument("--workload", default="glm1m", help="datagen config name")
     ap.add_argument("--no-baseline", action="store_true", help="skip the score-table baseline")
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
+    ap.add_argument("--no-backward", action="store_true",
+                    help="skip timing the indexer backward at the replayed entries")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
     ap.add_argument("--copy-probe", type=int, default=0, metavar="BYTES",
                     help="only run one plain device-to-device copy of BYTES bytes (calibrates "
@@ -220,6 +231,37 @@ def main() -> int:
         if not same:
             log("WARNING: baseline result differs from hytopk_select")
 
+    bwd = None
+    if not args.no_backward and not fp8:
+        log("backward at the replayed entries (dq, dw, dk)")
+        bws = torch.empty(hk.backward_workspace_bytes(q, k, w, inp.k), dtype=torch.uint8, device=dev)
+        gen = torch.Generator(device=dev)
+        gen.manual_seed(1234)
+        dsc = torch.randn((inp.n, inp.k), generator=gen, dtype=torch.float32, device=dev)
+        outs = {"dq": torch.empty((inp.n, inp.H, inp.d), dtype=torch.float32, device=dev),
+                "dw": torch.empty((inp.n, inp.H), dtype=torch.float32, device=dev),
+                "dk": torch.empty((inp.L, inp.d), dtype=torch.float32, device=dev)}
+        for _ in range(max(1, args.warmup)):
+            hk.backward(q, k, w, idx, dsc, workspace=bws, out=outs)
+        torch.cuda.synchronize()
+        hk.trace_enable(True)
+        bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
+               for _ in range(args.steps)]
+        for a, b in bev:
+            a.record()
+            hk.backward(q, k, w, idx, dsc, workspace=bws, out=outs)
+            b.record()
+        torch.cuda.synchronize()
+        bph = hk.trace_read()
+        hk.trace_enable(False)
+        bms = float(np.median([a.elapsed_time(b) for a, b in bev]))
+        abytes = backward_bytes(inp.L, inp.n, inp.H, inp.d, inp.k)
+        bwd = {"ms": round(bms, 4), "algorithmic_bytes": abytes,
+               "gbs": round(abytes / (bms * 1e-3) / 1e9, 1),
+               "hbm_frac": round(abytes / (bms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
+               "phases_ms": {nm: round(t / args.steps, 4) for nm, (c, t) in bph.items()}}
+        del bws, outs
+
     cpu = None
     if not args.no_cpu:
         log("cpu baseline: oracle on a bounded sample")
@@ -251,6 +293,7 @@ def main() -> int:
         "baseline_ms": None if baseline_ms is None else round(baseline_ms, 3),
         "baseline_over_select": None if baseline_ms is None else round(baseline_ms / select_ms, 3),
         "phases_ms": {name: round(t / max(1, c), 4) for name, (c, t) in phases.items()},
+        "backward": bwd,
         "stats": stats,
         "roofline": {"bound": "mfma", "kernel": "score_tile_kernel (fused score+compare+compact)",
                      "achieved": None if achieved is None else round(achieved, 2), "peak": peak,

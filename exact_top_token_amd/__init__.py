@@ -15,14 +15,15 @@ __all__ = [
     "Problem", "Params", "Stats", "load_library", "library_path", "select", "replay",
     "baseline_select", "select_workspace_bytes", "baseline_workspace_bytes", "HytopkError",
     "EXPORTS", "BF16", "FP8_E4M3", "PATH_AUTO", "PATH_ROWS_ALL", "trace_enable", "trace_read",
+    "backward", "backward_workspace_bytes",
 ]
 
 BF16, FP8_E4M3 = 0, 1
 PATH_AUTO, PATH_ROWS_ALL = 0, 1
 EXPORTS = (
     "hytopk_select_workspace", "hytopk_baseline_workspace", "hytopk_select", "hytopk_replay",
-    "hytopk_baseline_select", "hytopk_status_string", "hytopk_last_error",
-    "hytopk_trace_enable", "hytopk_trace_read",
+    "hytopk_baseline_select", "hytopk_backward_workspace", "hytopk_backward",
+    "hytopk_status_string", "hytopk_last_error", "hytopk_trace_enable", "hytopk_trace_read",
 )
 
 
@@ -90,6 +91,10 @@ def load_library():
     lib.hytopk_replay.restype = ctypes.c_int
     lib.hytopk_baseline_select.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
     lib.hytopk_baseline_select.restype = ctypes.c_int
+    lib.hytopk_backward_workspace.argtypes = [P(Problem)]
+    lib.hytopk_backward_workspace.restype = sz
+    lib.hytopk_backward.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
+    lib.hytopk_backward.restype = ctypes.c_int
     lib.hytopk_status_string.argtypes = [ctypes.c_int]
     lib.hytopk_status_string.restype = ctypes.c_char_p
     lib.hytopk_last_error.argtypes = []
@@ -245,3 +250,36 @@ def baseline_select(q, k, w, topk: int, *, q_scale=None, k_scale=None, q_start=N
                                       _ptr(k_scale), _ptr(w), _ptr(idx), _ptr(score),
                                       _ptr(workspace), workspace.numel(), _stream(q)))
     return idx, score
+
+
+def backward_workspace_bytes(q, k, w, topk: int, q_start=None) -> int:
+    lib = load_library()
+    return int(lib.hytopk_backward_workspace(ctypes.byref(_problem(q, k, w, topk, q_start))))
+
+
+def backward(q, k, w, idx, d_score, *, q_scale=None, k_scale=None, q_start=None,
+             want=("dq", "dw", "dk"), workspace=None, out=None):
+    """Indexer backward at the replayed entries idx [n][k] with upstream
+    gradient d_score [n][k] (fp32).  Returns a dict with the requested fp32
+    gradients: dq [n][H][d], dw [n][H], dk [L][d]."""
+    import torch
+    lib = load_library()
+    prob = _problem(q, k, w, idx.shape[1], q_start)
+    for t, name in ((idx, "idx"), (d_score, "d_score")):
+        if tuple(t.shape) != (prob.n, prob.k) or not t.is_contiguous() or not t.is_cuda:
+            raise ValueError(f"{name} must be a contiguous [n][k] tensor on the GPU")
+    if idx.dtype != torch.int32 or d_score.dtype != torch.float32:
+        raise ValueError("idx must be int32 and d_score float32")
+    res = dict(out or {})
+    shapes = {"dq": (prob.n, prob.H, prob.d), "dw": (prob.n, prob.H), "dk": (prob.L, prob.d)}
+    for name in want:
+        if name not in res:
+            res[name] = torch.empty(shapes[name], dtype=torch.float32, device=q.device)
+    if "dk" in res and workspace is None:
+        need = int(lib.hytopk_backward_workspace(ctypes.byref(prob)))
+        workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _check(lib.hytopk_backward(ctypes.byref(prob), _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale),
+                               _ptr(w), _ptr(idx), _ptr(d_score), _ptr(res.get("dq")),
+                               _ptr(res.get("dw")), _ptr(res.get("dk")), _ptr(workspace),
+                               0 if workspace is None else workspace.numel(), _stream(q)))
+    return res

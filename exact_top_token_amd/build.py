@@ -19,7 +19,7 @@ CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 BUILD = os.path.join(ROOT, "_build")
 LIB = os.path.join(PKG, "libhytopk.so")
-SOURCES = ["api.hip", "score.hip", "gather.hip", "radix.hip"]
+SOURCES = ["api.hip", "score.hip", "gather.hip", "radix.hip", "backward.hip"]
 ARCH = os.environ.get("HYTOPK_ARCH", "gfx950")
 
 FLAGS = [

@@ -199,6 +199,32 @@ void splits(int64_t nq, int64_t maxctx, int& nsplit, int& split_len) {
   split_len = (int)len;
 }
 
+// Backward workspace: u rows of one chunk of queries, then the sort buffers.
+constexpr int64_t kBwdChunkBytes = int64_t(1) << 31;
+
+struct BwdLayout {
+  int64_t chunk;
+  size_t u, k0, v0, k1, v1, hist, heads, nheads, total;
+};
+
+BwdLayout bwd_layout(const hytopk_problem* p) {
+  BwdLayout l{};
+  const int64_t row = (int64_t)p->k * p->d * 4;  // u bytes per query
+  l.chunk = std::max<int64_t>(1, std::min<int64_t>(p->n, kBwdChunkBytes / row));
+  const int64_t N = l.chunk * p->k;
+  size_t off = 0;
+  l.u = off; off = align_up(off + (size_t)N * p->d * 4);
+  l.k0 = off; off = align_up(off + (size_t)N * 4);
+  l.v0 = off; off = align_up(off + (size_t)N * 4);
+  l.k1 = off; off = align_up(off + (size_t)N * 4);
+  l.v1 = off; off = align_up(off + (size_t)N * 4);
+  l.hist = off; off = align_up(off + hk::bwd_sort_hist_count(N) * 4);
+  l.heads = off; off = align_up(off + (size_t)N * 4);
+  l.nheads = off; off = align_up(off + 4);
+  l.total = off;
+  return l;
+}
+
 hk::ScoreArgs score_args(const hytopk_problem* p, const void* q, const float* qs, const void* k,
                          const float* ks, const float* w) {
   hk::ScoreArgs a{};
@@ -448,6 +474,73 @@ int hytopk_baseline_select(const hytopk_problem* p, const void* q, const float* 
   return rows_path(p, base, nullptr, 0, (int)p->n, p->q_start + p->n,
                    static_cast<float*>(workspace), out_idx, out_score,
                    static_cast<hipStream_t>(stream));
+}
+
+
+size_t hytopk_backward_workspace(const hytopk_problem* p) {
+  if (check_problem(p) != HYTOPK_OK) return 0;
+  return bwd_layout(p).total;
+}
+
+int hytopk_backward(const hytopk_problem* p, const void* q, const float* q_scale, const void* k,
+                    const float* k_scale, const float* w, const int32_t* idx,
+                    const float* d_score, float* dq, float* dw, float* dk, void* workspace,
+                    size_t workspace_bytes, void* stream) {
+  g_err.clear();
+  int rc = check_problem(p);
+  if (rc) return rc;
+  if (p->dtype != HYTOPK_BF16) return fail(HYTOPK_EUNSUPPORTED, "backward supports bf16 only");
+  if ((rc = check_inputs(p, q, q_scale, k, k_scale, w))) return rc;
+  if (!idx || !d_score) return fail(HYTOPK_EINVAL, "idx and d_score must be non-NULL");
+  const BwdLayout l = bwd_layout(p);
+  if (dk && (rc = check_ws(workspace, workspace_bytes, l.total))) return rc;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  const int K = p->k, D = p->d;
+  char* ws = static_cast<char*>(workspace);
+  float* u = dk ? reinterpret_cast<float*>(ws + l.u) : nullptr;
+  if (dk) {
+    Span sp("bwd_dk", s);
+    HK_HIP(hk::launch_fill_zero(dk, p->L * (int64_t)D, s), "dk clear");
+  }
+  for (int64_t q0 = 0; q0 < p->n; q0 += l.chunk) {
+    const int nq = (int)std::min<int64_t>(l.chunk, p->n - q0);
+    hk::BwdArgs a{};
+    a.q = static_cast<const uint16_t*>(q);
+    a.k = static_cast<const uint16_t*>(k);
+    a.w = w;
+    a.idx = idx;
+    a.dsc = d_score;
+    a.dq = dq;
+    a.dw = dw;
+    a.u = u;
+    a.L = (int)p->L;
+    a.H = p->H;
+    a.topk = K;
+    a.q0 = (int)q0;
+    a.nq = nq;
+    {
+      Span sp("bwd_query", s);
+      HK_HIP(hk::launch_bwd_query(a, D, s), "backward query launch");
+    }
+    if (dk) {
+      hk::DkArgs b{};
+      b.idx = idx + q0 * K;
+      b.L = (int)p->L;
+      b.N = nq * K;
+      b.k0 = reinterpret_cast<uint32_t*>(ws + l.k0);
+      b.v0 = reinterpret_cast<uint32_t*>(ws + l.v0);
+      b.k1 = reinterpret_cast<uint32_t*>(ws + l.k1);
+      b.v1 = reinterpret_cast<uint32_t*>(ws + l.v1);
+      b.hist = reinterpret_cast<uint32_t*>(ws + l.hist);
+      b.heads = reinterpret_cast<int*>(ws + l.heads);
+      b.nheads = reinterpret_cast<int*>(ws + l.nheads);
+      b.u = u;
+      b.dk = dk;
+      Span sp("bwd_dk", s);
+      HK_HIP(hk::launch_bwd_dk(b, D, s), "backward dk launch");
+    }
+  }
+  return HYTOPK_OK;
 }
 
 }  // extern "C"

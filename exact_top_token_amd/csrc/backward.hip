@@ -1,0 +1,497 @@
+// Indexer backward at the replayed entries ("HyScale sparse-attention
+// training -- Selection without a score table", key-observation paragraph:
+// the indexer's loss reads only the scores at the selected entries and the
+// top-k choice carries no gradient).  Given dI[t, j], the upstream gradient
+// of the replayed score I(t, idx[t, j]), with c[h, j] = q[t, h] . k[idx[t, j]]
+// and ReLU'(c) = [c > 0]:
+//   dw[t, h]    = sum_j dI[t, j] * max(c[h, j], 0)
+//   dq[t, h, :] = w[t, h] * sum_j dI[t, j] [c[h, j] > 0] k[idx[t, j], :]
+//   u[t, j, :]  = sum_h dI[t, j] w[t, h] [c[h, j] > 0] q[t, h, :]
+//   dk[s, :]    = sum over the entries (t, j) with idx[t, j] = s of u[t, j, :]
+//
+// bwd_query_kernel: one workgroup (4 waves) per query, the query's keys in
+// tiles of 32.  Wave w owns heads 16w .. 16w + 15.  It forms c with the query
+// as the A operand (lane: 4 heads x 1 key) and c^T with the same registers
+// swapped (lane: 1 head x 4 keys), so each layout feeds the next MFMA without
+// a transpose:
+//   * c^T's layout is dq's A operand (head rows, keys along K); dq's B
+//     operand reads the tile transposed in LDS (dims x keys);
+//   * c's layout gives G = dI w [c > 0] per (key, 4 heads), stored to LDS as
+//     key rows; every wave then forms u for its quarter of the dims with
+//     Q^T (dims x heads, held in registers) as the A operand.
+// The MFMA operands in the gradient products are bf16, so each fp32 factor
+// is split into a round-to-nearest bf16 high part and the bf16 of the
+// remainder (hi + lo carries 16 significant bits); both parts are
+// multiplied against exact bf16 key / query values and accumulated in fp32.
+//
+// dk: the u rows of a chunk of queries go to a buffer; a stable LSD radix
+// sort of (key position, entry) pairs groups them by key with entries in
+// query-then-slot order; one wave per key sums its rows in that order and
+// adds them to dk.  Chunks run in order, so dk is bitwise reproducible.
+#include "common.h"
+#include "launch.h"
+
+namespace hk {
+
+constexpr int kBwdThreads = 256;
+constexpr int kBwdTK = 32;     // keys per tile
+constexpr int kBwdDepth = 2;   // tiles of key rows in flight (registers)
+constexpr int kKtW = kBwdTK + 8;  // transposed tile row (bf16), padded
+constexpr int kGtW = 64 + 8;      // G row (bf16): 64 heads, padded
+
+__device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
+  const __bf16 h = (__bf16)x;
+  const __bf16 l = (__bf16)(x - (float)h);
+  hi = __builtin_bit_cast(uint16_t, h);
+  lo = __builtin_bit_cast(uint16_t, l);
+}
+
+__device__ __forceinline__ bf16x8 pack8(const uint32_t (&v)[8]) {
+  u32x4 p;
+  p[0] = v[0] | (v[1] << 16);
+  p[1] = v[2] | (v[3] << 16);
+  p[2] = v[4] | (v[5] << 16);
+  p[3] = v[6] | (v[7] << 16);
+  return __builtin_bit_cast(bf16x8, p);
+}
+
+__device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, const f32x4& c) {
+  return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+}
+
+template <int D>
+__global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
+  constexpr int NCH = D / 8;   // 16-byte chunks per key row
+  constexpr int KS = D / 32;   // k-steps of the c products
+  constexpr int NDB = D / 16;  // dim blocks of dq
+  constexpr int UDB = D / 64;  // dim blocks of u per wave (a wave owns D / 4 dims)
+  constexpr int CPT = kBwdTK * NCH / kBwdThreads;  // row chunks per thread per tile
+  static_assert(CPT >= 1 && kBwdTK * NCH % kBwdThreads == 0, "tile split");
+
+  __shared__ __attribute__((aligned(16))) uint16_t krow[2][kBwdTK * D];
+  __shared__ __attribute__((aligned(16))) uint16_t kt[2][D * kKtW];
+  __shared__ __attribute__((aligned(16))) uint16_t gt[2][2][kBwdTK * kGtW];
+  extern __shared__ int dyn[];
+
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
+  const int qi = a.q0 + blockIdx.x;  // query index in [0, n)
+  const int K = a.topk, H = a.H;
+  const int ntile = (K + kBwdTK - 1) / kBwdTK;
+  int* ids = dyn;                                          // [ntile * 32] key or -1
+  float* dI = reinterpret_cast<float*>(dyn + ntile * kBwdTK);  // [ntile * 32]
+
+  for (int j = tid; j < ntile * kBwdTK; j += kBwdThreads) {
+    int key = j < K ? a.idx[(int64_t)qi * K + j] : -1;
+    if (key < 0 || key >= a.L) key = -1;  // padding, never dereferenced
+    ids[j] = key;
+    dI[j] = key >= 0 ? a.dsc[(int64_t)qi * K + j] : 0.0f;
+  }
+
+  // Query fragments of this wave's heads: A operand of c, B operand of c^T.
+  bf16x8 qa[KS];
+  {
+    const int h = 16 * wave + c16;
+    const uint16_t* src = a.q + ((int64_t)qi * H + (h < H ? h : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks)
+      qa[ks] = h < H ? *reinterpret_cast<const bf16x8*>(src + (4 * ks + g) * 8) : bf16x8{};
+  }
+  // Q^T fragments for u: dim rows wave * D/4 + 16 udb + c16, heads 8g + 32hs + e.
+  bf16x8 qt[UDB][2];
+#pragma unroll
+  for (int udb = 0; udb < UDB; ++udb) {
+    const int i = wave * (D / 4) + 16 * udb + c16;
+#pragma unroll
+    for (int hs = 0; hs < 2; ++hs) {
+      uint32_t v[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int h = 8 * g + 32 * hs + e;
+        v[e] = h < H ? a.q[((int64_t)qi * H + h) * D + i] : 0u;
+      }
+      qt[udb][hs] = pack8(v);
+    }
+  }
+  float wv[4];
+#pragma unroll
+  for (int r = 0; r < 4; ++r) {
+    const int h = 16 * wave + 4 * g + r;
+    wv[r] = h < H ? a.w[(int64_t)qi * H + h] : 0.0f;
+  }
+  f32x4 dqa[NDB];
+#pragma unroll
+  for (int db = 0; db < NDB; ++db) dqa[db] = f32x4{0.f, 0.f, 0.f, 0.f};
+  float dwa[4] = {0.f, 0.f, 0.f, 0.f};
+  __syncthreads();  // ids / dI staged
+
+  u32x4 pf[kBwdDepth][CPT];
+  auto gather = [&](int tile, int slot) {
+#pragma unroll
+    for (int v = 0; v < CPT; ++v) {
+      const int c = tid + kBwdThreads * v, j = c / NCH, cc = c % NCH;
+      const int key = tile < ntile ? ids[tile * kBwdTK + j] : -1;
+      pf[slot][v] = key >= 0 ? *reinterpret_cast<const u32x4*>(a.k + (int64_t)key * D + cc * 8)
+                             : u32x4{0u, 0u, 0u, 0u};
+    }
+  };
+  auto stage = [&](int slot, int buf) {
+#pragma unroll
+    for (int v = 0; v < CPT; ++v) {
+      const int c = tid + kBwdThreads * v, j = c / NCH, cc = c % NCH;
+      *reinterpret_cast<u32x4*>(&krow[buf][j * D + ((cc ^ (j & (NCH - 1))) * 8)]) = pf[slot][v];
+#pragma unroll
+      for (int e = 0; e < 8; ++e)
+        kt[buf][(cc * 8 + e) * kKtW + j] = (uint16_t)(pf[slot][v][e >> 1] >> (16 * (e & 1)));
+    }
+  };
+
+#pragma unroll
+  for (int s = 0; s < kBwdDepth; ++s) gather(s, s);
+
+  static_assert(kBwdDepth == 2, "slot and LDS buffer share the tile parity");
+  for (int t0 = 0; t0 < ntile; t0 += kBwdDepth)
+#pragma unroll
+  for (int slot = 0; slot < kBwdDepth; ++slot) {
+    const int t = t0 + slot, buf = slot;
+    if (t >= ntile) break;  // uniform
+    stage(slot, buf);
+    gather(t + kBwdDepth, slot);
+    __syncthreads();  // key tile t in krow / kt
+
+    f32x4 c[2], ct[2];
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      c[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+      ct[blk] = f32x4{0.f, 0.f, 0.f, 0.f};
+      const int j = 16 * blk + c16;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        const bf16x8 kb = *reinterpret_cast<const bf16x8*>(
+            &krow[buf][j * D + (((4 * ks + g) ^ (j & (NCH - 1))) * 8)]);
+        c[blk] = mfma_bf16(qa[ks], kb, c[blk]);   // lane: heads 4g + r, key j
+        ct[blk] = mfma_bf16(kb, qa[ks], ct[blk]);  // lane: keys 16 blk + 4g + r, head c16
+      }
+    }
+    // dw partials and G = dI w [c > 0] (key rows, for u)
+#pragma unroll
+    for (int blk = 0; blk < 2; ++blk) {
+      const int j = 16 * blk + c16;
+      const float di = dI[t * kBwdTK + j];
+      uint32_t hi[4], lo[4];
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const float cv = c[blk][r];
+        dwa[r] = __builtin_fmaf(di, __builtin_fmaxf(cv, 0.0f), dwa[r]);
+        split_bf16(cv > 0.0f ? di * wv[r] : 0.0f, hi[r], lo[r]);
+      }
+      uint2* dh = reinterpret_cast<uint2*>(&gt[buf][0][j * kGtW + 16 * wave + 4 * g]);
+      uint2* dl = reinterpret_cast<uint2*>(&gt[buf][1][j * kGtW + 16 * wave + 4 * g]);
+      *dh = uint2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
+      *dl = uint2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
+    }
+    // G' = dI [c > 0] in c^T's layout: dq's A operand (K slot 4 blk + r of
+    // lane group g is key 16 blk + 4g + r)
+    bf16x8 gqh, gql;
+    {
+      uint32_t vh[8], vl[8];
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          uint32_t h, l;
+          split_bf16(dI[t * kBwdTK + 16 * blk + 4 * g + r], h, l);
+          const bool on = ct[blk][r] > 0.0f;
+          vh[4 * blk + r] = on ? h : 0u;
+          vl[4 * blk + r] = on ? l : 0u;
+        }
+      }
+      gqh = pack8(vh);
+      gql = pack8(vl);
+    }
+    __syncthreads();  // G rows of all heads in gt
+
+    // dq[h, i] += sum_j G'[h, j] k[j, i]; B operand: dims x keys from kt
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+      const uint16_t* row = &kt[buf][(16 * db + c16) * kKtW];
+      const uint2 p0 = *reinterpret_cast<const uint2*>(row + 4 * g);
+      const uint2 p1 = *reinterpret_cast<const uint2*>(row + 16 + 4 * g);
+      const bf16x8 kb = __builtin_bit_cast(bf16x8, u32x4{p0.x, p0.y, p1.x, p1.y});
+      dqa[db] = mfma_bf16(gqh, kb, dqa[db]);
+      dqa[db] = mfma_bf16(gql, kb, dqa[db]);
+    }
+    // u^T[i, j] = sum_h Q^T[i, h] G[h, j] for this wave's dims
+    if (a.u) {
+#pragma unroll
+      for (int blk = 0; blk < 2; ++blk) {
+        const int j = 16 * blk + c16;
+        bf16x8 gh[2], gl[2];
+#pragma unroll
+        for (int hs = 0; hs < 2; ++hs) {
+          gh[hs] = *reinterpret_cast<const bf16x8*>(&gt[buf][0][j * kGtW + 8 * g + 32 * hs]);
+          gl[hs] = *reinterpret_cast<const bf16x8*>(&gt[buf][1][j * kGtW + 8 * g + 32 * hs]);
+        }
+        const int jg = t * kBwdTK + j;
+        const bool valid = ids[jg] >= 0;
+#pragma unroll
+        for (int udb = 0; udb < UDB; ++udb) {
+          f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+          for (int hs = 0; hs < 2; ++hs) {
+            acc = mfma_bf16(qt[udb][hs], gh[hs], acc);
+            acc = mfma_bf16(qt[udb][hs], gl[hs], acc);
+          }
+          if (valid)  // lane: dims wave * D/4 + 16 udb + 4g + r of key slot jg
+            *reinterpret_cast<f32x4*>(a.u + ((int64_t)blockIdx.x * K + jg) * D + wave * (D / 4) +
+                                      16 * udb + 4 * g) = acc;
+        }
+      }
+    }
+  }
+
+  if (a.dq) {
+#pragma unroll
+    for (int db = 0; db < NDB; ++db) {
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int h = 16 * wave + 4 * g + r;
+        if (h < H) a.dq[((int64_t)qi * H + h) * D + 16 * db + c16] = wv[r] * dqa[db][r];
+      }
+    }
+  }
+  if (a.dw) {
+#pragma unroll
+    for (int r = 0; r < 4; ++r) {
+      float v = dwa[r];
+      v += __shfl_xor(v, 1);
+      v += __shfl_xor(v, 2);
+      v += __shfl_xor(v, 4);
+      v += __shfl_xor(v, 8);
+      const int h = 16 * wave + 4 * g + r;
+      if (c16 == 0 && h < H) a.dw[(int64_t)qi * H + h] = v;
+    }
+  }
+}
+
+template <int D>
+static hipError_t bwd_query_d(const BwdArgs& a, hipStream_t s) {
+  const int ntile = (a.topk + kBwdTK - 1) / kBwdTK;
+  const size_t dyn = (size_t)ntile * kBwdTK * 8;
+  hipError_t e = hipFuncSetAttribute((const void*)bwd_query_kernel<D>,
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+  if (e != hipSuccess) return e;
+  hipLaunchKernelGGL(bwd_query_kernel<D>, dim3((unsigned)a.nq), dim3(kBwdThreads), dyn, s, a);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_query(const BwdArgs& a, int d, hipStream_t s) {
+  if (a.nq <= 0) return hipSuccess;
+  if (d == 64) return bwd_query_d<64>(a, s);
+  if (d == 128) return bwd_query_d<128>(a, s);
+  return hipErrorInvalidValue;
+}
+
+// ----------------------------------------------------------------- dk
+
+constexpr int kRsThreads = 256;
+constexpr int kRsItems = 16;
+constexpr int kRsTile = kRsThreads * kRsItems;  // entries per sort tile
+
+int rs_tiles(int64_t N) { return (int)((N + kRsTile - 1) / kRsTile); }
+
+// (key position, entry) pairs of a chunk; positions outside [0, L) become L
+// (they sort last and are skipped).  Also clears the segment-head counter.
+__global__ void bwd_pairs_kernel(const int* idx, int L, int N, uint32_t* keys, uint32_t* vals,
+                                 int* nheads) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  if (e == 0) *nheads = 0;
+  if (e >= N) return;
+  const int s = idx[e];
+  keys[e] = (s >= 0 && s < L) ? (uint32_t)s : (uint32_t)L;
+  vals[e] = (uint32_t)e;
+}
+
+// Digit counts of one tile, stored digit-major: hist[d * ntiles + tile].
+__global__ void __launch_bounds__(kRsThreads) rs_hist_kernel(const uint32_t* keys, int N, int shift,
+                                                             int ntiles, uint32_t* hist) {
+  __shared__ int cnt[256];
+  const int tid = threadIdx.x;
+  cnt[tid] = 0;
+  __syncthreads();
+  const int base = blockIdx.x * kRsTile;
+  for (int it = 0; it < kRsItems; ++it) {
+    const int e = base + it * kRsThreads + tid;
+    if (e < N) atomicAdd(&cnt[(keys[e] >> shift) & 255u], 1);
+  }
+  __syncthreads();
+  hist[(int64_t)tid * ntiles + blockIdx.x] = (uint32_t)cnt[tid];
+}
+
+// Exclusive scan of m counts in place (one workgroup of 1024 threads; each
+// thread owns a contiguous run).
+__global__ void __launch_bounds__(1024) rs_scan_kernel(uint32_t* v, int m) {
+  __shared__ uint32_t wsum[16];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int per = (m + 1023) / 1024;
+  const int b = tid * per, e = min(m, b + per);
+  uint32_t s = 0;
+  for (int i = b; i < e; ++i) s += v[i];
+  const uint32_t pre = (uint32_t)wave_prefix_excl((int)s);
+  if (lane == 63) wsum[wave] = pre + s;
+  __syncthreads();
+  uint32_t off = 0;
+  for (int w = 0; w < wave; ++w) off += wsum[w];
+  uint32_t run = off + pre;
+  for (int i = b; i < e; ++i) {
+    const uint32_t x = v[i];
+    v[i] = run;
+    run += x;
+  }
+}
+
+// Stable scatter of one tile by its 8-bit digit.  Entries are taken in
+// rounds of 256 (round, wave, lane order = input order); within a wave the
+// entries with the same digit are found with 8 bit-plane ballots.
+__global__ void __launch_bounds__(kRsThreads) rs_scatter_kernel(const uint32_t* kin,
+                                                                const uint32_t* vin, uint32_t* kout,
+                                                                uint32_t* vout, int N, int shift,
+                                                                int ntiles, const uint32_t* hist) {
+  __shared__ uint32_t base[256];
+  __shared__ uint32_t wc[kRsThreads / kWave][256];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  base[tid] = hist[(int64_t)tid * ntiles + blockIdx.x];
+#pragma unroll
+  for (int w = 0; w < kRsThreads / kWave; ++w) wc[w][tid] = 0u;
+  __syncthreads();
+  for (int it = 0; it < kRsItems; ++it) {
+    const int e = blockIdx.x * kRsTile + it * kRsThreads + tid;
+    const bool valid = e < N;
+    const uint32_t key = valid ? kin[e] : 0u;
+    const uint32_t val = valid ? vin[e] : 0u;
+    const uint32_t dg = (key >> shift) & 255u;
+    uint64_t peers = __ballot(valid);
+#pragma unroll
+    for (int bit = 0; bit < 8; ++bit) {
+      const bool on = (dg >> bit) & 1u;
+      const uint64_t bb = __ballot(on);
+      peers &= on ? bb : ~bb;
+    }
+    const int rank = __popcll(peers & lt);
+    if (valid && rank == 0) wc[wave][dg] = (uint32_t)__popcll(peers);
+    __syncthreads();
+    if (valid) {
+      uint32_t off = base[dg] + (uint32_t)rank;
+      for (int w = 0; w < wave; ++w) off += wc[w][dg];
+      kout[off] = key;
+      vout[off] = val;
+    }
+    __syncthreads();
+    uint32_t s = 0;
+#pragma unroll
+    for (int w = 0; w < kRsThreads / kWave; ++w) {
+      s += wc[w][tid];
+      wc[w][tid] = 0u;
+    }
+    base[tid] += s;
+    __syncthreads();
+  }
+}
+
+// First entry of every key's run in the sorted order (valid keys only).
+__global__ void seg_heads_kernel(const uint32_t* keys, int N, uint32_t L, int* heads, int* nheads) {
+  const int e = blockIdx.x * blockDim.x + threadIdx.x;
+  const int lane = threadIdx.x & 63;
+  bool h = false;
+  if (e < N) {
+    const uint32_t k = keys[e];
+    h = k < L && (e == 0 || keys[e - 1] != k);
+  }
+  const uint64_t m = __ballot(h);
+  int b = 0;
+  if (lane == 0 && m) b = atomicAdd(nheads, __popcll(m));
+  b = __shfl(b, 0);
+  if (h) heads[b + __popcll(m & (lane == 0 ? 0ull : (~0ull >> (64 - lane))))] = e;
+}
+
+// One wave per key run: dk[s] += the run's u rows, summed in sorted order.
+template <int D>
+__global__ void __launch_bounds__(256) dk_accum_kernel(const uint32_t* keys, const uint32_t* vals,
+                                                       int N, const int* heads, const int* nheads,
+                                                       const float* u, float* dk) {
+  constexpr int V = D / 64;
+  const int lane = threadIdx.x & 63;
+  const int nw = gridDim.x * (blockDim.x >> 6);
+  const int total = *nheads;
+  for (int h = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); h < total; h += nw) {
+    const int p = heads[h];
+    const uint32_t s = keys[p];
+    float acc[V];
+#pragma unroll
+    for (int v = 0; v < V; ++v) acc[v] = 0.0f;
+    for (int q = p; q < N && keys[q] == s; ++q) {
+      const float* row = u + (int64_t)vals[q] * D;
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] += row[lane + 64 * v];
+    }
+    float* out = dk + (int64_t)s * D;
+#pragma unroll
+    for (int v = 0; v < V; ++v) out[lane + 64 * v] += acc[v];
+  }
+}
+
+__global__ void fill_zero_kernel(float* p, int64_t n) {
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n;
+       i += (int64_t)gridDim.x * blockDim.x)
+    p[i] = 0.0f;
+}
+
+size_t bwd_sort_hist_count(int64_t N) { return (size_t)256 * rs_tiles(N); }
+
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  const int64_t want = (n + 255) / 256;
+  const int nb = (int)(want < 8192 ? want : 8192);
+  hipLaunchKernelGGL(fill_zero_kernel, dim3(nb), dim3(256), 0, s, p, n);
+  return hipGetLastError();
+}
+
+hipError_t launch_bwd_dk(const DkArgs& a, int d, hipStream_t s) {
+  const int N = a.N;
+  if (N <= 0) return hipSuccess;
+  const int nb = (N + 255) / 256;
+  hipLaunchKernelGGL(bwd_pairs_kernel, dim3(nb), dim3(256), 0, s, a.idx, a.L, N, a.k0, a.v0,
+                     a.nheads);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int ntiles = rs_tiles(N);
+  int bits = 0;
+  while (bits < 32 && ((uint64_t)a.L >> bits) != 0) ++bits;  // keys lie in [0, L]
+  uint32_t *ki = a.k0, *vi = a.v0, *ko = a.k1, *vo = a.v1;
+  for (int shift = 0; shift < bits; shift += 8) {
+    hipLaunchKernelGGL(rs_hist_kernel, dim3(ntiles), dim3(kRsThreads), 0, s, ki, N, shift, ntiles,
+                       a.hist);
+    hipLaunchKernelGGL(rs_scan_kernel, dim3(1), dim3(1024), 0, s, a.hist, 256 * ntiles);
+    hipLaunchKernelGGL(rs_scatter_kernel, dim3(ntiles), dim3(kRsThreads), 0, s, ki, vi, ko, vo, N,
+                       shift, ntiles, a.hist);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    uint32_t* t = ki; ki = ko; ko = t;
+    t = vi; vi = vo; vo = t;
+  }
+  hipLaunchKernelGGL(seg_heads_kernel, dim3(nb), dim3(256), 0, s, ki, N, (uint32_t)a.L, a.heads,
+                     a.nheads);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int grid = 2048;
+  if (d == 64) {
+    hipLaunchKernelGGL(dk_accum_kernel<64>, dim3(grid), dim3(256), 0, s, ki, vi, N, a.heads,
+                       a.nheads, a.u, a.dk);
+  } else if (d == 128) {
+    hipLaunchKernelGGL(dk_accum_kernel<128>, dim3(grid), dim3(256), 0, s, ki, vi, N, a.heads,
+                       a.nheads, a.u, a.dk);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
+}
+
+}  // namespace hk

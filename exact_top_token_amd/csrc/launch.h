@@ -106,4 +106,43 @@ hipError_t launch_row_topk(const float* rows, int64_t row_stride, const int* qli
 // LDS bytes cand_select needs for this cap / k (the host checks the limit).
 size_t cand_select_lds_bytes(int cap, int topk);
 
+
+// Indexer backward at the replayed entries (backward.hip).
+struct BwdArgs {
+  const uint16_t* q;   // bf16 bits [n][H][d]
+  const uint16_t* k;   // bf16 bits [L][d]
+  const float* w;      // [n][H]
+  const int* idx;      // [n][topk]
+  const float* dsc;    // [n][topk] upstream gradient of each replayed score
+  float* dq;           // [n][H][d] or null
+  float* dw;           // [n][H] or null
+  float* u;            // [nq * topk][d] dk rows of this chunk's entries, or null
+  int L;
+  int H;
+  int topk;
+  int q0;              // first query of the chunk
+  int nq;              // queries in the chunk
+};
+
+hipError_t launch_bwd_query(const BwdArgs& a, int d, hipStream_t s);
+
+struct DkArgs {
+  const int* idx;      // the chunk's [nq][topk] indices (entry e = row-major position)
+  int L;
+  int N;               // entries in the chunk
+  uint32_t* k0;        // [N] sort ping-pong buffers
+  uint32_t* v0;
+  uint32_t* k1;
+  uint32_t* v1;
+  uint32_t* hist;      // [bwd_sort_hist_count(N)]
+  int* heads;          // [N]
+  int* nheads;         // [1]
+  const float* u;      // [N][d]
+  float* dk;           // [L][d], accumulated
+};
+
+hipError_t launch_bwd_dk(const DkArgs& a, int d, hipStream_t s);
+hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
+size_t bwd_sort_hist_count(int64_t N);
+
 }  // namespace hk

@@ -151,13 +151,40 @@ int hytopk_baseline_select(const hytopk_problem* p, const void* q, const float* 
                            int32_t* out_idx, float* out_score,
                            void* workspace, size_t workspace_bytes, void* stream);
 
+/* Workspace bytes of hytopk_backward (0 on invalid input): the dk rows of one
+ * chunk of queries plus the buffers that group them by key.  The chunk size
+ * depends only on the problem (about 2 GiB of rows), so results do not depend
+ * on the workspace a caller passes. */
+size_t hytopk_backward_workspace(const hytopk_problem* p);
+
+/* Indexer backward at the replayed entries (HyScale explainer, key-observation
+ * paragraph: the indexer's loss reads only the scores at the selected entries,
+ * and the top-k choice itself carries no gradient).  With d_score [n][k] fp32
+ * the upstream gradient of the replayed scores I(q_start + i, idx[i][j]),
+ * c = q[i][h] . k[idx[i][j]] and ReLU'(c) = [c > 0] (0 at c == 0):
+ *   dw [n][H]    fp32: dw[i][h]    = sum_j d_score[i][j] * max(c, 0)
+ *   dq [n][H][d] fp32: dq[i][h][:] = w[i][h] * sum_j d_score[i][j] [c > 0] k[idx[i][j]][:]
+ *   dk [L][d]    fp32: dk[s][:]    = sum over entries with idx[i][j] = s of
+ *                                    sum_h d_score[i][j] w[i][h] [c > 0] q[i][h][:]
+ * Every output is fully written (dk is 0 for keys no query selected); any of
+ * dq, dw, dk may be NULL to skip it (dk NULL skips the workspace traffic).
+ * Indices outside [0, L) are padding and contribute nothing.  dk is summed in
+ * a fixed order (query ascending, then slot), so results are bitwise
+ * reproducible.  bf16 inputs only (HYTOPK_EUNSUPPORTED for fp8).  Products
+ * use bf16 MFMA with every fp32 factor split into two bf16 parts (16
+ * significant bits) and fp32 accumulation. */
+int hytopk_backward(const hytopk_problem* p, const void* q, const float* q_scale,
+                    const void* k, const float* k_scale, const float* w, const int32_t* idx,
+                    const float* d_score, float* dq, float* dw, float* dk,
+                    void* workspace, size_t workspace_bytes, void* stream);
+
 const char* hytopk_status_string(int status);
 const char* hytopk_last_error(void);  /* thread-local; "" when none */
 
 /* Kernel tracing.  While enabled, every launch the library makes is bracketed
  * by a pair of hipEvents recorded on the caller's stream, and the elapsed time
  * is accumulated per phase name ("sample_tau", "score_compact", "check",
- * "cand_select", "score_rows", "row_topk", "replay").  Process-wide; not for
+ * "cand_select", "score_rows", "row_topk", "replay", "bwd_query", "bwd_dk").  Process-wide; not for
  * use with concurrent calls on different streams. */
 typedef struct {
   char name[32];

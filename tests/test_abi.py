@@ -93,3 +93,23 @@ def test_bad_params_are_rejected(lib):
     for kw in (dict(cap=20000), dict(m_max=1 << 15), dict(force_path=5), dict(oversample=-1)):
         prm = hk.Params(**kw)
         assert lib.hytopk_select_workspace(ctypes.byref(p), ctypes.byref(prm)) == 0
+
+
+def test_backward_workspace_and_argument_errors(lib):
+    p = _prob()
+    ws = lib.hytopk_backward_workspace(ctypes.byref(p))
+    # one chunk of 2 GiB of dk rows (2048 queries x 2048 entries x 128 fp32)
+    # plus the key-grouping buffers
+    assert (2 << 30) <= ws < (2 << 30) + (256 << 20) and ws % 256 == 0
+    fake = ctypes.c_void_p(0x1000)
+    args = [fake, None, fake, None, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None]
+    # fp8 -> unsupported; NULL idx / d_score -> invalid; small workspace with dk -> -3
+    p8 = _prob(dtype=hk.FP8_E4M3)
+    assert lib.hytopk_backward(ctypes.byref(p8), *args) == -2
+    a = list(args); a[5] = None
+    assert lib.hytopk_backward(ctypes.byref(p), *a) == -1
+    a = list(args); a[11] = 16
+    assert lib.hytopk_backward(ctypes.byref(p), *a) == -3
+    bad = _prob(k=4097)
+    assert lib.hytopk_backward_workspace(ctypes.byref(bad)) == 0
+    assert lib.hytopk_backward(ctypes.byref(bad), *args) == -2
