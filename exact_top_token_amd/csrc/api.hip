@@ -200,27 +200,26 @@ void splits(int64_t nq, int64_t maxctx, int& nsplit, int& split_len) {
 }
 
 // Backward workspace: u rows of one chunk of queries, then the sort buffers.
-constexpr int64_t kBwdChunkBytes = int64_t(1) << 31;
+constexpr int64_t kBwdChunkBytes = int64_t(1) << 33;
 
 struct BwdLayout {
   int64_t chunk;
-  size_t u, k0, v0, k1, v1, hist, heads, nheads, total;
+  size_t u, k0, v0, k1, v1, hist, total;
 };
 
 BwdLayout bwd_layout(const hytopk_problem* p) {
   BwdLayout l{};
-  const int64_t row = (int64_t)p->k * p->d * 4;  // u bytes per query
+  const int64_t kp = hk::bwd_padded_k(p->k);
+  const int64_t row = kp * p->d * 4;  // u bytes per query
   l.chunk = std::max<int64_t>(1, std::min<int64_t>(p->n, kBwdChunkBytes / row));
   const int64_t N = l.chunk * p->k;
   size_t off = 0;
-  l.u = off; off = align_up(off + (size_t)N * p->d * 4);
+  l.u = off; off = align_up(off + (size_t)(l.chunk * kp) * p->d * 4);
   l.k0 = off; off = align_up(off + (size_t)N * 4);
   l.v0 = off; off = align_up(off + (size_t)N * 4);
   l.k1 = off; off = align_up(off + (size_t)N * 4);
   l.v1 = off; off = align_up(off + (size_t)N * 4);
   l.hist = off; off = align_up(off + hk::bwd_sort_hist_count(N) * 4);
-  l.heads = off; off = align_up(off + (size_t)N * 4);
-  l.nheads = off; off = align_up(off + 4);
   l.total = off;
   return l;
 }
@@ -504,6 +503,21 @@ int hytopk_backward(const hytopk_problem* p, const void* q, const float* q_scale
   }
   for (int64_t q0 = 0; q0 < p->n; q0 += l.chunk) {
     const int nq = (int)std::min<int64_t>(l.chunk, p->n - q0);
+    const uint32_t *sorted_keys = nullptr, *sorted_rows = nullptr;
+    if (dk) {
+      hk::DkArgs b{};
+      b.idx = idx + q0 * K;
+      b.L = (int)p->L;
+      b.N = nq * K;
+      b.topk = K;
+      b.k0 = reinterpret_cast<uint32_t*>(ws + l.k0);
+      b.v0 = reinterpret_cast<uint32_t*>(ws + l.v0);
+      b.k1 = reinterpret_cast<uint32_t*>(ws + l.k1);
+      b.v1 = reinterpret_cast<uint32_t*>(ws + l.v1);
+      b.hist = reinterpret_cast<uint32_t*>(ws + l.hist);
+      Span sp("bwd_dk", s);
+      HK_HIP(hk::launch_bwd_sort(b, &sorted_keys, &sorted_rows, s), "backward key sort launch");
+    }
     hk::BwdArgs a{};
     a.q = static_cast<const uint16_t*>(q);
     a.k = static_cast<const uint16_t*>(k);
@@ -523,21 +537,10 @@ int hytopk_backward(const hytopk_problem* p, const void* q, const float* q_scale
       HK_HIP(hk::launch_bwd_query(a, D, s), "backward query launch");
     }
     if (dk) {
-      hk::DkArgs b{};
-      b.idx = idx + q0 * K;
-      b.L = (int)p->L;
-      b.N = nq * K;
-      b.k0 = reinterpret_cast<uint32_t*>(ws + l.k0);
-      b.v0 = reinterpret_cast<uint32_t*>(ws + l.v0);
-      b.k1 = reinterpret_cast<uint32_t*>(ws + l.k1);
-      b.v1 = reinterpret_cast<uint32_t*>(ws + l.v1);
-      b.hist = reinterpret_cast<uint32_t*>(ws + l.hist);
-      b.heads = reinterpret_cast<int*>(ws + l.heads);
-      b.nheads = reinterpret_cast<int*>(ws + l.nheads);
-      b.u = u;
-      b.dk = dk;
       Span sp("bwd_dk", s);
-      HK_HIP(hk::launch_bwd_dk(b, D, s), "backward dk launch");
+      HK_HIP(hk::launch_bwd_segments(sorted_keys, sorted_rows, nq * K, (int)p->L, u, dk, q0 > 0,
+                                     D, s),
+             "backward dk launch");
     }
   }
   return HYTOPK_OK;

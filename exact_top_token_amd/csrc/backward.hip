@@ -24,10 +24,12 @@
 // remainder (hi + lo carries 16 significant bits); both parts are
 // multiplied against exact bf16 key / query values and accumulated in fp32.
 //
-// dk: the u rows of a chunk of queries go to a buffer; a stable LSD radix
-// sort of (key position, entry) pairs groups them by key with entries in
-// query-then-slot order; one wave per key sums its rows in that order and
-// adds them to dk.  Chunks run in order, so dk is bitwise reproducible.
+// dk: the u rows of a chunk of queries go to a buffer (query-major); a stable
+// LSD radix sort of (key position, row) pairs groups them by key with entries
+// in query-then-slot order; waves sum each key's rows in that order and add
+// the sum to dk.  Chunks run in order, so dk is bitwise reproducible.
+#include <type_traits>
+
 #include "common.h"
 #include "launch.h"
 
@@ -36,7 +38,13 @@ namespace hk {
 constexpr int kBwdThreads = 256;
 constexpr int kBwdTK = 32;     // keys per tile
 constexpr int kBwdDepth = 2;   // tiles of key rows in flight (registers)
-constexpr int kKtW = kBwdTK + 8;  // transposed tile row (bf16), padded
+constexpr int kKtW = kBwdTK + 4;  // transposed tile row (bf16), padded
+
+// Transposed tile: row i (a dim) holds the 32 keys in 8 groups of 4; group
+// kg sits at slot kg ^ kt_swz(i).  With 36-element rows this makes both the
+// staging writes (32 dim quads x 2 key groups per wave) and the dq operand
+// reads (16 dims x 2 groups per lane group) free of LDS bank conflicts.
+__device__ __forceinline__ int kt_swz(int i) { return ((i >> 4) ^ (i >> 5)) & 7; }
 constexpr int kGtW = 64 + 8;      // G row (bf16): 64 heads, padded
 
 __device__ __forceinline__ void split_bf16(float x, uint32_t& hi, uint32_t& lo) {
@@ -59,14 +67,12 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, con
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D>
+template <int D, bool WITH_U>
 __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
   constexpr int NCH = D / 8;   // 16-byte chunks per key row
   constexpr int KS = D / 32;   // k-steps of the c products
   constexpr int NDB = D / 16;  // dim blocks of dq
   constexpr int UDB = D / 64;  // dim blocks of u per wave (a wave owns D / 4 dims)
-  constexpr int CPT = kBwdTK * NCH / kBwdThreads;  // row chunks per thread per tile
-  static_assert(CPT >= 1 && kBwdTK * NCH % kBwdThreads == 0, "tile split");
 
   __shared__ __attribute__((aligned(16))) uint16_t krow[2][kBwdTK * D];
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][D * kKtW];
@@ -77,10 +83,14 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
   const int qi = a.q0 + blockIdx.x;  // query index in [0, n)
   const int K = a.topk, H = a.H;
   const int ntile = (K + kBwdTK - 1) / kBwdTK;
-  int* ids = dyn;                                          // [ntile * 32] key or -1
-  float* dI = reinterpret_cast<float*>(dyn + ntile * kBwdTK);  // [ntile * 32]
+  // tiles processed: an even count (two LDS buffers, two register slots),
+  // plus kBwdDepth tiles of padding that the prefetch reads past the end
+  const int ntile2 = (ntile + 1) & ~1;
+  const int nslot = (ntile2 + kBwdDepth) * kBwdTK;
+  int* ids = dyn;                                   // [nslot] key or -1
+  float* dI = reinterpret_cast<float*>(dyn + nslot);  // [nslot]
 
-  for (int j = tid; j < ntile * kBwdTK; j += kBwdThreads) {
+  for (int j = tid; j < nslot; j += kBwdThreads) {
     int key = j < K ? a.idx[(int64_t)qi * K + j] : -1;
     if (key < 0 || key >= a.L) key = -1;  // padding, never dereferenced
     ids[j] = key;
@@ -124,24 +134,45 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
   float dwa[4] = {0.f, 0.f, 0.f, 0.f};
   __syncthreads();  // ids / dI staged
 
-  u32x4 pf[kBwdDepth][CPT];
+  // Staging: thread t < NBLK moves a 4 keys x 4 dims block of the tile:
+  // keys 4 kg .. 4 kg + 3, dims 4 q4 .. 4 q4 + 3 (8-byte global loads; a row's
+  // 256 bytes come from 32 consecutive lanes).
+  constexpr int NQ4 = D / 4;
+  constexpr int NBLK = (kBwdTK / 4) * NQ4;
+  static_assert(NBLK <= kBwdThreads, "one block per thread");
+  const bool stager = NBLK == kBwdThreads || tid < NBLK;
+  const int kg = tid / NQ4, q4 = tid % NQ4;
+  uint2 pf[kBwdDepth][4];
   auto gather = [&](int tile, int slot) {
+    if (!stager) return;
 #pragma unroll
-    for (int v = 0; v < CPT; ++v) {
-      const int c = tid + kBwdThreads * v, j = c / NCH, cc = c % NCH;
-      const int key = tile < ntile ? ids[tile * kBwdTK + j] : -1;
-      pf[slot][v] = key >= 0 ? *reinterpret_cast<const u32x4*>(a.k + (int64_t)key * D + cc * 8)
-                             : u32x4{0u, 0u, 0u, 0u};
+    for (int v = 0; v < 4; ++v) {
+      // unconditional load (padding reads row 0 and is zeroed when staged):
+      // no branch around the load and no use of it before the stage keeps
+      // the wait counts of the pipeline exact
+      const int key = ids[tile * kBwdTK + 4 * kg + v];
+      pf[slot][v] = *reinterpret_cast<const uint2*>(a.k + (int64_t)(key >= 0 ? key : 0) * D + 4 * q4);
     }
   };
-  auto stage = [&](int slot, int buf) {
+  auto stage = [&](int tile, int slot, int buf) {
+    if (!stager) return;
+    uint2 x[4];
 #pragma unroll
-    for (int v = 0; v < CPT; ++v) {
-      const int c = tid + kBwdThreads * v, j = c / NCH, cc = c % NCH;
-      *reinterpret_cast<u32x4*>(&krow[buf][j * D + ((cc ^ (j & (NCH - 1))) * 8)]) = pf[slot][v];
+    for (int v = 0; v < 4; ++v) {
+      const int j = 4 * kg + v;
+      x[v] = pf[slot][v];
+      if (ids[tile * kBwdTK + j] < 0) x[v] = uint2{0u, 0u};
+      *reinterpret_cast<uint2*>(&krow[buf][j * D + (((q4 >> 1) ^ (j & (NCH - 1))) * 8) + 4 * (q4 & 1)]) = x[v];
+    }
 #pragma unroll
-      for (int e = 0; e < 8; ++e)
-        kt[buf][(cc * 8 + e) * kKtW + j] = (uint16_t)(pf[slot][v][e >> 1] >> (16 * (e & 1)));
+    for (int e = 0; e < 4; ++e) {
+      const int i = 4 * q4 + e;
+      const int sh = 16 * (e & 1);
+      uint32_t b[4];
+#pragma unroll
+      for (int v = 0; v < 4; ++v) b[v] = ((e < 2 ? x[v].x : x[v].y) >> sh) & 0xFFFFu;
+      *reinterpret_cast<uint2*>(&kt[buf][i * kKtW + ((kg ^ kt_swz(i)) * 4)]) =
+          uint2{b[0] | (b[1] << 16), b[2] | (b[3] << 16)};
     }
   };
 
@@ -149,12 +180,9 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
   for (int s = 0; s < kBwdDepth; ++s) gather(s, s);
 
   static_assert(kBwdDepth == 2, "slot and LDS buffer share the tile parity");
-  for (int t0 = 0; t0 < ntile; t0 += kBwdDepth)
-#pragma unroll
-  for (int slot = 0; slot < kBwdDepth; ++slot) {
-    const int t = t0 + slot, buf = slot;
-    if (t >= ntile) break;  // uniform
-    stage(slot, buf);
+  auto tile_body = [&](const int t, auto slotc) {
+    constexpr int slot = decltype(slotc)::value, buf = slot;
+    stage(t, slot, buf);
     gather(t + kBwdDepth, slot);
     __syncthreads();  // key tile t in krow / kt
 
@@ -213,15 +241,16 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
     // dq[h, i] += sum_j G'[h, j] k[j, i]; B operand: dims x keys from kt
 #pragma unroll
     for (int db = 0; db < NDB; ++db) {
-      const uint16_t* row = &kt[buf][(16 * db + c16) * kKtW];
-      const uint2 p0 = *reinterpret_cast<const uint2*>(row + 4 * g);
-      const uint2 p1 = *reinterpret_cast<const uint2*>(row + 16 + 4 * g);
+      const int i = 16 * db + c16;
+      const uint16_t* row = &kt[buf][i * kKtW];
+      const uint2 p0 = *reinterpret_cast<const uint2*>(row + ((g ^ kt_swz(i)) * 4));
+      const uint2 p1 = *reinterpret_cast<const uint2*>(row + (((4 + g) ^ kt_swz(i)) * 4));
       const bf16x8 kb = __builtin_bit_cast(bf16x8, u32x4{p0.x, p0.y, p1.x, p1.y});
       dqa[db] = mfma_bf16(gqh, kb, dqa[db]);
       dqa[db] = mfma_bf16(gql, kb, dqa[db]);
     }
     // u^T[i, j] = sum_h Q^T[i, h] G[h, j] for this wave's dims
-    if (a.u) {
+    if constexpr (WITH_U) {
 #pragma unroll
       for (int blk = 0; blk < 2; ++blk) {
         const int j = 16 * blk + c16;
@@ -232,7 +261,6 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
           gl[hs] = *reinterpret_cast<const bf16x8*>(&gt[buf][1][j * kGtW + 8 * g + 32 * hs]);
         }
         const int jg = t * kBwdTK + j;
-        const bool valid = ids[jg] >= 0;
 #pragma unroll
         for (int udb = 0; udb < UDB; ++udb) {
           f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -241,12 +269,17 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
             acc = mfma_bf16(qt[udb][hs], gh[hs], acc);
             acc = mfma_bf16(qt[udb][hs], gl[hs], acc);
           }
-          if (valid)  // lane: dims wave * D/4 + 16 udb + 4g + r of key slot jg
-            *reinterpret_cast<f32x4*>(a.u + ((int64_t)blockIdx.x * K + jg) * D + wave * (D / 4) +
-                                      16 * udb + 4 * g) = acc;
+          // lane: dims wave * D/4 + 16 udb + 4g + r of key slot jg; every
+          // slot of the padded tiles has a row (padding rows are never read)
+          *reinterpret_cast<f32x4*>(a.u + ((int64_t)blockIdx.x * ntile2 * kBwdTK + jg) * D +
+                                    wave * (D / 4) + 16 * udb + 4 * g) = acc;
         }
       }
     }
+  };
+  for (int t0 = 0; t0 < ntile2; t0 += kBwdDepth) {
+    tile_body(t0, std::integral_constant<int, 0>{});
+    tile_body(t0 + 1, std::integral_constant<int, 1>{});
   }
 
   if (a.dq) {
@@ -273,21 +306,23 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
   }
 }
 
-template <int D>
+template <int D, bool WITH_U>
 static hipError_t bwd_query_d(const BwdArgs& a, hipStream_t s) {
   const int ntile = (a.topk + kBwdTK - 1) / kBwdTK;
-  const size_t dyn = (size_t)ntile * kBwdTK * 8;
-  hipError_t e = hipFuncSetAttribute((const void*)bwd_query_kernel<D>,
+  const size_t dyn = (size_t)(((ntile + 1) & ~1) + kBwdDepth) * kBwdTK * 8;
+  hipError_t e = hipFuncSetAttribute((const void*)bwd_query_kernel<D, WITH_U>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL(bwd_query_kernel<D>, dim3((unsigned)a.nq), dim3(kBwdThreads), dyn, s, a);
+  hipLaunchKernelGGL((bwd_query_kernel<D, WITH_U>), dim3((unsigned)a.nq), dim3(kBwdThreads), dyn, s,
+                     a);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_query(const BwdArgs& a, int d, hipStream_t s) {
   if (a.nq <= 0) return hipSuccess;
-  if (d == 64) return bwd_query_d<64>(a, s);
-  if (d == 128) return bwd_query_d<128>(a, s);
+  const bool u = a.u != nullptr;
+  if (d == 64) return u ? bwd_query_d<64, true>(a, s) : bwd_query_d<64, false>(a, s);
+  if (d == 128) return u ? bwd_query_d<128, true>(a, s) : bwd_query_d<128, false>(a, s);
   return hipErrorInvalidValue;
 }
 
@@ -300,15 +335,16 @@ constexpr int kRsTile = kRsThreads * kRsItems;  // entries per sort tile
 int rs_tiles(int64_t N) { return (int)((N + kRsTile - 1) / kRsTile); }
 
 // (key position, entry) pairs of a chunk; positions outside [0, L) become L
-// (they sort last and are skipped).  Also clears the segment-head counter.
-__global__ void bwd_pairs_kernel(const int* idx, int L, int N, uint32_t* keys, uint32_t* vals,
-                                 int* nheads) {
+// (they sort last and are skipped).
+// The value is the entry's u row: query-major, slots padded to an even
+// number of key tiles.
+__global__ void bwd_pairs_kernel(const int* idx, int L, int N, int topk, int kpad, uint32_t* keys,
+                                 uint32_t* vals) {
   const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  if (e == 0) *nheads = 0;
   if (e >= N) return;
   const int s = idx[e];
   keys[e] = (s >= 0 && s < L) ? (uint32_t)s : (uint32_t)L;
-  vals[e] = (uint32_t)e;
+  vals[e] = (uint32_t)((e / topk) * kpad + e % topk);
 }
 
 // Digit counts of one tile, stored digit-major: hist[d * ntiles + tile].
@@ -327,26 +363,30 @@ __global__ void __launch_bounds__(kRsThreads) rs_hist_kernel(const uint32_t* key
   hist[(int64_t)tid * ntiles + blockIdx.x] = (uint32_t)cnt[tid];
 }
 
-// Exclusive scan of m counts in place (one workgroup of 1024 threads; each
-// thread owns a contiguous run).
-__global__ void __launch_bounds__(1024) rs_scan_kernel(uint32_t* v, int m) {
-  __shared__ uint32_t wsum[16];
+// Exclusive scan of one digit's per-tile counts (workgroup d scans
+// hist[d][0..ntiles) in place) and that digit's total in tot[d].
+__global__ void __launch_bounds__(kRsThreads) rs_scan_kernel(uint32_t* hist, int ntiles,
+                                                             uint32_t* tot) {
+  __shared__ uint32_t wsum[kRsThreads / kWave];
+  __shared__ uint32_t carry;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int per = (m + 1023) / 1024;
-  const int b = tid * per, e = min(m, b + per);
-  uint32_t s = 0;
-  for (int i = b; i < e; ++i) s += v[i];
-  const uint32_t pre = (uint32_t)wave_prefix_excl((int)s);
-  if (lane == 63) wsum[wave] = pre + s;
+  uint32_t* v = hist + (int64_t)blockIdx.x * ntiles;
+  if (tid == 0) carry = 0u;
   __syncthreads();
-  uint32_t off = 0;
-  for (int w = 0; w < wave; ++w) off += wsum[w];
-  uint32_t run = off + pre;
-  for (int i = b; i < e; ++i) {
-    const uint32_t x = v[i];
-    v[i] = run;
-    run += x;
+  for (int b0 = 0; b0 < ntiles; b0 += kRsThreads) {
+    const int i = b0 + tid;
+    const uint32_t x = i < ntiles ? v[i] : 0u;
+    const uint32_t pre = (uint32_t)wave_prefix_excl((int)x);
+    if (lane == 63) wsum[wave] = pre + x;
+    __syncthreads();
+    uint32_t off = carry;
+    for (int w = 0; w < wave; ++w) off += wsum[w];
+    if (i < ntiles) v[i] = off + pre;
+    __syncthreads();
+    if (tid == kRsThreads - 1) carry = off + pre + x;
+    __syncthreads();
   }
+  if (tid == 0) tot[blockIdx.x] = carry;
 }
 
 // Stable scatter of one tile by its 8-bit digit.  Entries are taken in
@@ -355,12 +395,23 @@ __global__ void __launch_bounds__(1024) rs_scan_kernel(uint32_t* v, int m) {
 __global__ void __launch_bounds__(kRsThreads) rs_scatter_kernel(const uint32_t* kin,
                                                                 const uint32_t* vin, uint32_t* kout,
                                                                 uint32_t* vout, int N, int shift,
-                                                                int ntiles, const uint32_t* hist) {
+                                                                int ntiles, const uint32_t* hist,
+                                                                const uint32_t* tot) {
   __shared__ uint32_t base[256];
   __shared__ uint32_t wc[kRsThreads / kWave][256];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
-  base[tid] = hist[(int64_t)tid * ntiles + blockIdx.x];
+  {
+    // entries of smaller digits (exclusive scan of the 256 digit totals)
+    const uint32_t x = tot[tid];
+    const uint32_t pre = (uint32_t)wave_prefix_excl((int)x);
+    if (lane == 63) wc[0][wave] = pre + x;
+    __syncthreads();
+    uint32_t off = 0u;
+    for (int w = 0; w < wave; ++w) off += wc[0][w];
+    __syncthreads();
+    base[tid] = off + pre + hist[(int64_t)tid * ntiles + blockIdx.x];
+  }
 #pragma unroll
   for (int w = 0; w < kRsThreads / kWave; ++w) wc[w][tid] = 0u;
   __syncthreads();
@@ -398,46 +449,76 @@ __global__ void __launch_bounds__(kRsThreads) rs_scatter_kernel(const uint32_t* 
   }
 }
 
-// First entry of every key's run in the sorted order (valid keys only).
-__global__ void seg_heads_kernel(const uint32_t* keys, int N, uint32_t L, int* heads, int* nheads) {
-  const int e = blockIdx.x * blockDim.x + threadIdx.x;
-  const int lane = threadIdx.x & 63;
-  bool h = false;
-  if (e < N) {
-    const uint32_t k = keys[e];
-    h = k < L && (e == 0 || keys[e - 1] != k);
-  }
-  const uint64_t m = __ballot(h);
-  int b = 0;
-  if (lane == 0 && m) b = atomicAdd(nheads, __popcll(m));
-  b = __shfl(b, 0);
-  if (h) heads[b + __popcll(m & (lane == 0 ? 0ull : (~0ull >> (64 - lane))))] = e;
-}
+// dk[s] (+)= the u rows of key s's run, summed in sorted (entry) order.  Wave
+// w owns the runs that START at sorted positions [64w, 64w + 64); the last of
+// them may continue past the window.  The wave walks its rows in order,
+// kDkBatch row loads in flight at a time, and flushes a run's sum when the
+// key changes (stored on the first chunk, added on later ones).
+constexpr int kDkBatch = 8;
 
-// One wave per key run: dk[s] += the run's u rows, summed in sorted order.
 template <int D>
-__global__ void __launch_bounds__(256) dk_accum_kernel(const uint32_t* keys, const uint32_t* vals,
-                                                       int N, const int* heads, const int* nheads,
-                                                       const float* u, float* dk) {
-  constexpr int V = D / 64;
+__global__ void __launch_bounds__(256) dk_segments_kernel(const uint32_t* keys, const uint32_t* vals,
+                                                          int N, uint32_t L, const float* u,
+                                                          float* dk, int accumulate) {
+  constexpr int V = D / 64;  // floats per lane per row
   const int lane = threadIdx.x & 63;
-  const int nw = gridDim.x * (blockDim.x >> 6);
-  const int total = *nheads;
-  for (int h = blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6); h < total; h += nw) {
-    const int p = heads[h];
-    const uint32_t s = keys[p];
-    float acc[V];
+  const int p0 = (blockIdx.x * (blockDim.x >> 6) + (threadIdx.x >> 6)) * 64;
+  if (p0 >= N) return;  // wave-uniform; no barrier in this kernel
+  const int p = p0 + lane;
+  const uint32_t kp = p < N ? keys[p] : 0xFFFFFFFFu;
+  const uint32_t kprev = p == 0 ? 0xFFFFFFFFu : (p <= N ? keys[p - 1] : 0xFFFFFFFFu);
+  const uint32_t myval = p < N ? vals[p] : 0u;
+  const uint64_t heads = __ballot(p < N && kp < L && kp != kprev);
+  if (!heads) return;
+  const int first = __builtin_ctzll(heads);
+  const uint32_t s_last = __shfl(kp, 63 - __builtin_clzll(heads));
+  uint32_t cur = __shfl(kp, first);
+  float acc[V];
 #pragma unroll
-    for (int v = 0; v < V; ++v) acc[v] = 0.0f;
-    for (int q = p; q < N && keys[q] == s; ++q) {
-      const float* row = u + (int64_t)vals[q] * D;
+  for (int v = 0; v < V; ++v) acc[v] = 0.0f;
+  auto flush = [&](uint32_t key) {
+    float* out = dk + (int64_t)key * D + V * lane;
 #pragma unroll
-      for (int v = 0; v < V; ++v) acc[v] += row[lane + 64 * v];
+    for (int v = 0; v < V; ++v) out[v] = accumulate ? out[v] + acc[v] : acc[v];
+  };
+  for (int x = p0 + first;; x += kDkBatch) {
+    uint32_t kb[kDkBatch], vb[kDkBatch];
+    bool own[kDkBatch];
+#pragma unroll
+    for (int b = 0; b < kDkBatch; ++b) {
+      const int xb = x + b;
+      if (xb - p0 < 64) {  // uniform: inside the window, from registers
+        kb[b] = __shfl(kp, xb - p0);
+        vb[b] = __shfl(myval, xb - p0);
+        own[b] = kb[b] < L;  // every valid run here started in the window
+      } else {             // past the window: only the last run continues
+        kb[b] = xb < N ? keys[xb] : 0xFFFFFFFFu;
+        own[b] = kb[b] == s_last;
+        vb[b] = own[b] ? vals[xb] : 0u;
+      }
     }
-    float* out = dk + (int64_t)s * D;
+    float r[kDkBatch][V];
 #pragma unroll
-    for (int v = 0; v < V; ++v) out[lane + 64 * v] += acc[v];
+    for (int b = 0; b < kDkBatch; ++b) {
+      const float* row = u + (int64_t)(own[b] ? vb[b] : 0u) * D + V * lane;
+#pragma unroll
+      for (int v = 0; v < V; ++v) r[b][v] = own[b] ? row[v] : 0.0f;
+    }
+#pragma unroll
+    for (int b = 0; b < kDkBatch; ++b) {
+      if (!own[b]) continue;  // uniform
+      if (kb[b] != cur) {
+        flush(cur);
+        cur = kb[b];
+#pragma unroll
+        for (int v = 0; v < V; ++v) acc[v] = 0.0f;
+      }
+#pragma unroll
+      for (int v = 0; v < V; ++v) acc[v] += r[b][v];
+    }
+    if (!own[kDkBatch - 1]) break;  // uniform: the wave's last run has ended
   }
+  flush(cur);
 }
 
 __global__ void fill_zero_kernel(float* p, int64_t n) {
@@ -446,7 +527,7 @@ __global__ void fill_zero_kernel(float* p, int64_t n) {
     p[i] = 0.0f;
 }
 
-size_t bwd_sort_hist_count(int64_t N) { return (size_t)256 * rs_tiles(N); }
+size_t bwd_sort_hist_count(int64_t N) { return (size_t)256 * rs_tiles(N) + 256; }
 
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   if (n <= 0) return hipSuccess;
@@ -456,42 +537,54 @@ hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s) {
   return hipGetLastError();
 }
 
-hipError_t launch_bwd_dk(const DkArgs& a, int d, hipStream_t s) {
+hipError_t launch_bwd_sort(const DkArgs& a, const uint32_t** sorted_keys,
+                           const uint32_t** sorted_rows, hipStream_t s) {
   const int N = a.N;
+  *sorted_keys = a.k0;
+  *sorted_rows = a.v0;
   if (N <= 0) return hipSuccess;
   const int nb = (N + 255) / 256;
-  hipLaunchKernelGGL(bwd_pairs_kernel, dim3(nb), dim3(256), 0, s, a.idx, a.L, N, a.k0, a.v0,
-                     a.nheads);
+  hipLaunchKernelGGL(bwd_pairs_kernel, dim3(nb), dim3(256), 0, s, a.idx, a.L, N, a.topk,
+                     bwd_padded_k(a.topk), a.k0, a.v0);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
   const int ntiles = rs_tiles(N);
   int bits = 0;
   while (bits < 32 && ((uint64_t)a.L >> bits) != 0) ++bits;  // keys lie in [0, L]
   uint32_t *ki = a.k0, *vi = a.v0, *ko = a.k1, *vo = a.v1;
+  uint32_t* tot = a.hist + (size_t)256 * ntiles;
   for (int shift = 0; shift < bits; shift += 8) {
     hipLaunchKernelGGL(rs_hist_kernel, dim3(ntiles), dim3(kRsThreads), 0, s, ki, N, shift, ntiles,
                        a.hist);
-    hipLaunchKernelGGL(rs_scan_kernel, dim3(1), dim3(1024), 0, s, a.hist, 256 * ntiles);
+    hipLaunchKernelGGL(rs_scan_kernel, dim3(256), dim3(kRsThreads), 0, s, a.hist, ntiles, tot);
     hipLaunchKernelGGL(rs_scatter_kernel, dim3(ntiles), dim3(kRsThreads), 0, s, ki, vi, ko, vo, N,
-                       shift, ntiles, a.hist);
+                       shift, ntiles, a.hist, tot);
     if ((e = hipGetLastError()) != hipSuccess) return e;
     uint32_t* t = ki; ki = ko; ko = t;
     t = vi; vi = vo; vo = t;
   }
-  hipLaunchKernelGGL(seg_heads_kernel, dim3(nb), dim3(256), 0, s, ki, N, (uint32_t)a.L, a.heads,
-                     a.nheads);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  const int grid = 2048;
+  *sorted_keys = ki;
+  *sorted_rows = vi;
+  return hipSuccess;
+}
+
+hipError_t launch_bwd_segments(const uint32_t* sorted_keys, const uint32_t* sorted_rows, int N,
+                               int L, const float* u, float* dk, bool accumulate, int d,
+                               hipStream_t s) {
+  if (N <= 0) return hipSuccess;
+  const int grid = (N + 255) / 256;  // 4 waves of 64 sorted positions each
   if (d == 64) {
-    hipLaunchKernelGGL(dk_accum_kernel<64>, dim3(grid), dim3(256), 0, s, ki, vi, N, a.heads,
-                       a.nheads, a.u, a.dk);
+    hipLaunchKernelGGL(dk_segments_kernel<64>, dim3(grid), dim3(256), 0, s, sorted_keys,
+                       sorted_rows, N, (uint32_t)L, u, dk, accumulate ? 1 : 0);
   } else if (d == 128) {
-    hipLaunchKernelGGL(dk_accum_kernel<128>, dim3(grid), dim3(256), 0, s, ki, vi, N, a.heads,
-                       a.nheads, a.u, a.dk);
+    hipLaunchKernelGGL(dk_segments_kernel<128>, dim3(grid), dim3(256), 0, s, sorted_keys,
+                       sorted_rows, N, (uint32_t)L, u, dk, accumulate ? 1 : 0);
   } else {
     return hipErrorInvalidValue;
   }
   return hipGetLastError();
 }
+
+int bwd_padded_k(int topk) { return (((topk + kBwdTK - 1) / kBwdTK + 1) & ~1) * kBwdTK; }
 
 }  // namespace hk

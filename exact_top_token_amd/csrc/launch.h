@@ -116,7 +116,7 @@ struct BwdArgs {
   const float* dsc;    // [n][topk] upstream gradient of each replayed score
   float* dq;           // [n][H][d] or null
   float* dw;           // [n][H] or null
-  float* u;            // [nq * topk][d] dk rows of this chunk's entries, or null
+  float* u;            // [nq * bwd_padded_k(topk)][d] dk rows of the chunk's entries, or null
   int L;
   int H;
   int topk;
@@ -129,19 +129,24 @@ hipError_t launch_bwd_query(const BwdArgs& a, int d, hipStream_t s);
 struct DkArgs {
   const int* idx;      // the chunk's [nq][topk] indices (entry e = row-major position)
   int L;
-  int N;               // entries in the chunk
+  int N;               // entries in the chunk (nq * topk)
+  int topk;
   uint32_t* k0;        // [N] sort ping-pong buffers
   uint32_t* v0;
   uint32_t* k1;
   uint32_t* v1;
-  uint32_t* hist;      // [bwd_sort_hist_count(N)]
-  int* heads;          // [N]
-  int* nheads;         // [1]
-  const float* u;      // [N][d]
-  float* dk;           // [L][d], accumulated
+  uint32_t* hist;      // [bwd_sort_hist_count(N)]: per-tile digit counts, digit totals
 };
 
-hipError_t launch_bwd_dk(const DkArgs& a, int d, hipStream_t s);
+// Groups the chunk's entries by key: stable sort of (key position, u row)
+// by key (padding last); returns the sorted keys and rows.
+hipError_t launch_bwd_sort(const DkArgs& a, const uint32_t** sorted_keys,
+                           const uint32_t** sorted_rows, hipStream_t s);
+// dk[s] = (or +=) the sum of the u rows of key s's run, in sorted order.
+hipError_t launch_bwd_segments(const uint32_t* sorted_keys, const uint32_t* sorted_rows, int N,
+                               int L, const float* u, float* dk, bool accumulate, int d,
+                               hipStream_t s);
+int bwd_padded_k(int topk);  // key slots per query in the u buffer
 hipError_t launch_fill_zero(float* p, int64_t n, hipStream_t s);
 size_t bwd_sort_hist_count(int64_t N);
 

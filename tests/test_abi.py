@@ -98,9 +98,9 @@ def test_bad_params_are_rejected(lib):
 def test_backward_workspace_and_argument_errors(lib):
     p = _prob()
     ws = lib.hytopk_backward_workspace(ctypes.byref(p))
-    # one chunk of 2 GiB of dk rows (2048 queries x 2048 entries x 128 fp32)
-    # plus the key-grouping buffers
-    assert (2 << 30) <= ws < (2 << 30) + (256 << 20) and ws % 256 == 0
+    # one chunk of 8 GiB of dk rows (all 8192 queries x 2048 entries x 128
+    # fp32) plus the key-grouping buffers (4 x 64 MiB and the digit counts)
+    assert (8 << 30) <= ws < (8 << 30) + (320 << 20) and ws % 256 == 0
     fake = ctypes.c_void_p(0x1000)
     args = [fake, None, fake, None, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None]
     # fp8 -> unsupported; NULL idx / d_score -> invalid; small workspace with dk -> -3
