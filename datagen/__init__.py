@@ -22,8 +22,11 @@ stress_a    1,048,576  8,192  64  128  2,048  clustered keys + planted failures
 stress_b    1,048,576  8,192  64  128  2,048  clustered keys + >64 planted failures
 ==========  =========  =====  ==  ===  =====  =====================================
 
-The queries always sit at the last n positions: query i has position
+By default the queries sit at the last n positions: query i has position
 ``q_start + i`` with ``q_start = L - n`` and sees keys ``0 .. q_start + i``.
+``make_packed`` builds the general form: several sequences packed into one key
+buffer, queries at chosen positions in any order, each seeing the keys from
+its own sequence's first key through its position (``q_pos``, ``q_first``).
 
 Draw order for every config: q, then k, then w, from
 ``numpy.random.default_rng(seed)``; fp32 draws are rounded to bf16 with
@@ -37,7 +40,7 @@ import math
 import numpy as np
 
 __all__ = [
-    "CONFIGS", "Inputs", "make", "make_custom", "f32_to_bf16_bits",
+    "CONFIGS", "Inputs", "make", "make_custom", "make_packed", "f32_to_bf16_bits",
     "f32_to_e4m3", "quantize_e4m3_per_row", "subset_queries",
 ]
 
@@ -57,7 +60,9 @@ class Inputs:
     ``q`` is ``[n][H][d]`` and ``k`` is ``[L][d]``: uint16 bf16 bit patterns, or
     uint8 OCP E4M3 codes when ``dtype == "fp8"`` (then ``q_scale[n]`` and
     ``k_scale[L]`` are the fp32 per-token dequantisation scales).  ``w`` is
-    ``[n][H]`` fp32.  Query ``i`` sits at position ``q_start + i``.
+    ``[n][H]`` fp32.  Query ``i`` sits at position ``q_start + i`` and sees
+    keys ``0 ..`` that position, unless ``q_pos`` / ``q_first`` (int32 ``[n]``)
+    give its position and the first key of its context explicitly.
     """
     name: str
     L: int
@@ -71,6 +76,8 @@ class Inputs:
     w: np.ndarray
     q_scale: np.ndarray | None = None
     k_scale: np.ndarray | None = None
+    q_pos: np.ndarray | None = None
+    q_first: np.ndarray | None = None
 
     @property
     def q_start(self) -> int:
@@ -160,6 +167,40 @@ def make(name: str) -> Inputs:
     cfg = CONFIGS[name]
     return make_custom(name, cfg["L"], cfg["n"], cfg["H"], cfg["d"], cfg["k"],
                        cfg["dtype"], cfg["dist"], cfg["seed"])
+
+
+def make_packed(name: str, seq_lens, chunks, H: int, d: int, k: int, dtype: str = "bf16",
+                dist: str = "normal", seed: int = 0, shuffle: bool = True) -> Inputs:
+    """Sequences of the given lengths packed back to back into one key buffer.
+    ``chunks`` lists (sequence, first local position, count) runs of query
+    positions; query order is shuffled (seeded) unless ``shuffle`` is False.
+    Values follow ``make_custom``'s recipes; draw order q, k, w, then the
+    shuffle."""
+    seq_lens = [int(x) for x in seq_lens]
+    starts = np.concatenate([[0], np.cumsum(seq_lens)[:-1]]).astype(np.int64)
+    pos, first = [], []
+    for sq, lp, cnt in chunks:
+        if not (0 <= lp and lp + cnt <= seq_lens[sq]):
+            raise ValueError("query run outside its sequence")
+        pos.extend(starts[sq] + lp + np.arange(cnt))
+        first.extend([starts[sq]] * cnt)
+    L, n = int(sum(seq_lens)), len(pos)
+    cfg = dict(L=L, n=n, H=H, d=d, k=k, dtype=dtype, dist=dist, seed=seed)
+    rng = np.random.default_rng(seed)
+    q32, k32, w = _draw(cfg, rng)
+    order = rng.permutation(n) if shuffle else np.arange(n)
+    q_pos = np.asarray(pos, dtype=np.int32)[order]
+    q_first = np.asarray(first, dtype=np.int32)[order]
+    if dtype == "bf16":
+        inp = Inputs(name, L, n, H, d, k, dtype, f32_to_bf16_bits(q32), f32_to_bf16_bits(k32), w)
+    elif dtype == "fp8":
+        qc, qs = quantize_e4m3_per_row(q32)
+        kc, ks = quantize_e4m3_per_row(k32)
+        inp = Inputs(name, L, n, H, d, k, dtype, qc, kc, w, qs, ks)
+    else:
+        raise ValueError(dtype)
+    inp.q_pos, inp.q_first = q_pos, q_first
+    return inp
 
 
 def subset_queries(n: int, count: int = 64, seed: int = 7, must: tuple[int, ...] = ()) -> np.ndarray:

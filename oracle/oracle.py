@@ -25,7 +25,8 @@ score table]:
 
 1. decode the stored inputs exactly to fp64 (bf16 bits; OCP E4M3 codes times
    their per-token fp32 scales; fp32 head weights);
-2. score every causal pair (query position t sees keys 0..t) with the
+2. score every causal pair (query position t sees keys 0..t; with packed
+   sequences, the keys from its own sequence's first key through t) with the
    learned-sparse-attention indexer I(t,s) = sum_h w[t,h] * ReLU(q[t,h] . k[s]).
    The pages do not print the indexer's formula; they say its scores are the
    same kind of work as attention scores [Explainer, contest] and that the
@@ -137,7 +138,17 @@ class Decoded:
         return q, inp.w[i].astype(np.float64)
 
     def position(self, i: int) -> int:
+        """Position t of query i: the explicit ``q_pos`` when given, else the
+        default q_start + i."""
+        if self.inp.q_pos is not None:
+            return int(self.inp.q_pos[i])
         return self.q_start + int(i)
+
+    def first(self, i: int) -> int:
+        """First key of query i's context (packed sequences), default 0."""
+        if self.inp.q_first is not None:
+            return int(self.inp.q_first[i])
+        return 0
 
 
 # ---------------------------------------------------------------------------
@@ -146,13 +157,16 @@ class Decoded:
 
 
 def score_row(dec: Decoded, i: int, chunk: int = 32768) -> np.ndarray:
-    """I(t, s) for query i (position t) and every key s = 0..t, in fp64."""
+    """I(t, s) for query i (position t) and every key s of its context,
+    first..t (first = 0 unless the query's sequence starts later), in fp64.
+    Entry j of the row is key first + j."""
     q, w = dec.query(i)
-    ctx = dec.position(i) + 1
+    lo = dec.first(i)
+    ctx = max(0, dec.position(i) + 1 - lo)
     out = np.empty(ctx, dtype=np.float64)
     for a in range(0, ctx, chunk):
         b = min(ctx, a + chunk)
-        dots = q @ dec.keys[a:b].T            # [H][b-a]  q[t,h] . k[s]
+        dots = q @ dec.keys[lo + a:lo + b].T  # [H][b-a]  q[t,h] . k[s]
         np.maximum(dots, 0.0, out=dots)       # ReLU
         out[a:b] = w @ dots                   # sum_h w[t,h] * ...
     return out
@@ -192,6 +206,7 @@ def select(inp, queries=None) -> tuple[np.ndarray, np.ndarray]:
     val = np.empty((qs.size, inp.k), dtype=np.float64)
     for r, i in enumerate(qs):
         idx[r], val[r] = exact_topk(score_row(dec, int(i)), inp.k)
+        idx[r][idx[r] >= 0] += dec.first(int(i))   # row entry j is key first + j
     return idx, val
 
 
