@@ -30,7 +30,7 @@ EXPORTS = (
 class Problem(ctypes.Structure):
     _fields_ = [("L", ctypes.c_int64), ("n", ctypes.c_int64), ("q_start", ctypes.c_int64),
                 ("H", ctypes.c_int32), ("d", ctypes.c_int32), ("k", ctypes.c_int32),
-                ("dtype", ctypes.c_int32)]
+                ("dtype", ctypes.c_int32), ("q_pos", ctypes.c_void_p), ("q_first", ctypes.c_void_p)]
 
 
 class Params(ctypes.Structure):
@@ -126,7 +126,8 @@ def _dtype_code(q) -> int:
     raise TypeError(f"q/k must be bfloat16 or float8_e4m3fn, got {q.dtype}")
 
 
-def _problem(q, k, w, topk: int, q_start) -> Problem:
+def _problem(q, k, w, topk: int, q_start, q_pos=None, q_first=None) -> Problem:
+    import torch
     n, H, d = q.shape
     L = k.shape[0]
     if k.shape[1] != d or tuple(w.shape) != (n, H):
@@ -134,7 +135,15 @@ def _problem(q, k, w, topk: int, q_start) -> Problem:
     for t in (q, k, w):
         if not t.is_cuda or not t.is_contiguous():
             raise ValueError("tensors must be contiguous and on the GPU")
-    return Problem(L, n, L - n if q_start is None else int(q_start), H, d, int(topk), _dtype_code(q))
+    for t in (q_pos, q_first):
+        if t is not None and (t.dtype != torch.int32 or tuple(t.shape) != (n,) or not t.is_cuda
+                              or not t.is_contiguous()):
+            raise ValueError("q_pos / q_first must be contiguous int32 [n] tensors on the GPU")
+    if q_start is None:
+        q_start = 0 if q_pos is not None else L - n
+    return Problem(L, n, int(q_start), H, d, int(topk), _dtype_code(q),
+                   None if q_pos is None else q_pos.data_ptr(),
+                   None if q_first is None else q_first.data_ptr())
 
 
 def _params(params) -> Params | None:
@@ -171,9 +180,10 @@ def trace_read() -> dict:
     return {arr[i].name.decode(): (arr[i].launches, arr[i].total_ms) for i in range(n)}
 
 
-def select_workspace_bytes(q, k, w, topk: int, q_start=None, params=None) -> int:
+def select_workspace_bytes(q, k, w, topk: int, q_start=None, params=None, q_pos=None,
+                           q_first=None) -> int:
     lib = load_library()
-    prob = _problem(q, k, w, topk, q_start)
+    prob = _problem(q, k, w, topk, q_start, q_pos, q_first)
     prm = _params(params)
     return int(lib.hytopk_select_workspace(ctypes.byref(prob), ctypes.byref(prm) if prm else None))
 
@@ -184,12 +194,14 @@ def baseline_workspace_bytes(q, k, w, topk: int, q_start=None) -> int:
 
 
 def select(q, k, w, topk: int, *, q_scale=None, k_scale=None, q_start=None, params=None,
-           workspace=None, out=None, with_stats: bool = False):
+           workspace=None, out=None, with_stats: bool = False, q_pos=None, q_first=None):
     """Exact top-k per query (HyTopK).  Returns (idx int32 [n][k], score fp32
-    [n][k]) and, with ``with_stats``, a dict of what the call did."""
+    [n][k]) and, with ``with_stats``, a dict of what the call did.  q_pos /
+    q_first (int32 [n] on the GPU, optional) give each query's position and
+    the first key of its context (packed sequences)."""
     import torch
     lib = load_library()
-    prob = _problem(q, k, w, topk, q_start)
+    prob = _problem(q, k, w, topk, q_start, q_pos, q_first)
     prm = _params(params)
     need = int(lib.hytopk_select_workspace(ctypes.byref(prob), ctypes.byref(prm) if prm else None))
     if need == 0:
@@ -233,11 +245,11 @@ def replay(q, k, w, idx, *, q_scale=None, k_scale=None, q_start=None, out=None):
 
 
 def baseline_select(q, k, w, topk: int, *, q_scale=None, k_scale=None, q_start=None,
-                    workspace=None, out=None):
+                    workspace=None, out=None, q_pos=None, q_first=None):
     """The materialise-then-top-k route (writes the n x L fp32 score table)."""
     import torch
     lib = load_library()
-    prob = _problem(q, k, w, topk, q_start)
+    prob = _problem(q, k, w, topk, q_start, q_pos, q_first)
     need = int(lib.hytopk_baseline_workspace(ctypes.byref(prob)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

@@ -103,7 +103,7 @@ struct Params {
 int check_problem(const hytopk_problem* p) {
   if (!p) return fail(HYTOPK_EINVAL, "problem is NULL");
   if (p->L <= 0 || p->n <= 0 || p->q_start < 0) return fail(HYTOPK_EINVAL, "L, n must be > 0 and q_start >= 0");
-  if (p->q_start + p->n > p->L) return fail(HYTOPK_EINVAL, "q_start + n > L");
+  if (!p->q_pos && p->q_start + p->n > p->L) return fail(HYTOPK_EINVAL, "q_start + n > L");
   if (p->L >= (int64_t(1) << 31)) return fail(HYTOPK_EUNSUPPORTED, "L >= 2^31");
   if (p->k <= 0) return fail(HYTOPK_EINVAL, "k must be > 0");
   if (p->k > kMaxK) return fail(HYTOPK_EUNSUPPORTED, "k > 2048");
@@ -234,8 +234,15 @@ hk::ScoreArgs score_args(const hytopk_problem* p, const void* q, const float* qs
   a.k_scale = ks;
   a.L = (int)p->L;
   a.q_start = (int)p->q_start;
+  a.qpos = p->q_pos;
+  a.qfirst = p->q_first;
   a.H = p->H;
   return a;
+}
+
+// Upper bound on the key range queries first..last-1 can see.
+int64_t ctx_bound(const hytopk_problem* p, int64_t last) {
+  return p->q_pos ? p->L : p->q_start + last;
 }
 
 // Score `nq` queries (qlist or q_offset..) into rows, then row top-k.
@@ -256,8 +263,8 @@ int rows_path(const hytopk_problem* p, const hk::ScoreArgs& base, const int* qli
   }
   {
     Span sp("row_topk", s);
-    HK_HIP(hk::launch_row_topk(rows, p->L, qlist, q_offset, nq, (int)p->q_start, p->k, (int)p->L,
-                               out_idx, out_score, s),
+    HK_HIP(hk::launch_row_topk(rows, p->L, qlist, q_offset, nq, p->q_pos, p->q_first,
+                               (int)p->q_start, p->k, (int)p->L, out_idx, out_score, s),
            "row top-k launch");
   }
   return HYTOPK_OK;
@@ -354,7 +361,7 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
   float* rows = reinterpret_cast<float*>(ws + l.rows);
   const bool fp8 = p->dtype == HYTOPK_FP8_E4M3;
   const int n = (int)p->n;
-  const int64_t maxctx = p->q_start + p->n;
+  const int64_t maxctx = ctx_bound(p, p->n);
   const hk::ScoreArgs base = score_args(p, q, q_scale, k, k_scale, w);
 
   hk::DevStats hs{};
@@ -364,6 +371,7 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
     hk::SampleArgs sa{};
     sa.q = base.q; sa.k = base.k; sa.w = w; sa.q_scale = q_scale; sa.k_scale = k_scale;
     sa.tau = tau; sa.L = (int)p->L; sa.q_start = (int)p->q_start; sa.n = n; sa.H = p->H;
+    sa.qpos = p->q_pos; sa.qfirst = p->q_first;
     sa.topk = p->k; sa.M = sample_count(p, r); sa.oversample = r.oversample;
     {
       Span sp("sample_tau", s);
@@ -383,7 +391,9 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
     }
     {
       Span sp("check", s);
-      HK_HIP(hk::launch_check(cnt, n, (int)p->q_start, p->k, r.cap, dst, failed, s), "check launch");
+      HK_HIP(hk::launch_check(cnt, n, p->q_pos, p->q_first, (int)p->q_start, (int)p->L, p->k,
+                              r.cap, dst, failed, s),
+             "check launch");
     }
     HK_HIP(hipMemcpyAsync(&hs, dst, sizeof(hs), hipMemcpyDeviceToHost, s), "stats copy");
     HK_HIP(hipStreamSynchronize(s), "stream sync");
@@ -395,8 +405,8 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
   if (path == 0) {
     {
       Span sp("cand_select", s);
-      HK_HIP(hk::launch_cand_select(cnt, cand, n, (int)p->q_start, p->k, r.cap, (int)p->L, out_idx,
-                                    out_score, s),
+      HK_HIP(hk::launch_cand_select(cnt, cand, n, p->q_pos, p->q_first, (int)p->q_start, p->k,
+                                    r.cap, (int)p->L, out_idx, out_score, s),
              "candidate select launch");
     }
     // Recovery: rescore only the flagged queries over their whole context.
@@ -409,7 +419,7 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
     // Full rescore: every query through the row path, in chunks of rows_n.
     for (int c0 = 0; c0 < n; c0 += l.rows_n) {
       const int nc = std::min(l.rows_n, n - c0);
-      rc = rows_path(p, base, nullptr, c0, nc, p->q_start + c0 + nc, rows, out_idx, out_score, s);
+      rc = rows_path(p, base, nullptr, c0, nc, ctx_bound(p, c0 + nc), rows, out_idx, out_score, s);
       if (rc) return rc;
     }
   }
@@ -470,7 +480,7 @@ int hytopk_baseline_select(const hytopk_problem* p, const void* q, const float* 
   if (!out_idx) return fail(HYTOPK_EINVAL, "out_idx is NULL");
   if ((rc = check_ws(workspace, workspace_bytes, hytopk_baseline_workspace(p)))) return rc;
   const hk::ScoreArgs base = score_args(p, q, q_scale, k, k_scale, w);
-  return rows_path(p, base, nullptr, 0, (int)p->n, p->q_start + p->n,
+  return rows_path(p, base, nullptr, 0, (int)p->n, ctx_bound(p, p->n),
                    static_cast<float*>(workspace), out_idx, out_score,
                    static_cast<hipStream_t>(stream));
 }

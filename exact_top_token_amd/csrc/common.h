@@ -28,6 +28,21 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 
 __device__ __forceinline__ int lane_id() { return __lane_id(); }
 
+// Keys of query q's context: lo..hi inclusive (empty when lo > hi).  The
+// explicit per-query position / first key when given (packed sequences,
+// arbitrary query positions), else position q_start + q and first key 0;
+// clamped to the key buffer [0, L).
+struct QRange {
+  int lo, hi;
+};
+
+__device__ __forceinline__ QRange query_range(const int* qpos, const int* qfirst, int q_start,
+                                              int L, int q) {
+  int hi = qpos ? qpos[q] : q_start + q;
+  int lo = qfirst ? qfirst[q] : 0;
+  return QRange{max(lo, 0), min(hi, L - 1)};
+}
+
 // Inclusive suffix sum across the 64 lanes of a wave: lane i gets sum_{j>=i} x_j.
 __device__ __forceinline__ int wave_suffix_sum(int x) {
   const int lane = lane_id();

@@ -166,7 +166,12 @@ __global__ void __launch_bounds__(kSampleThreads) sample_tau_kernel(SampleArgs a
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4;
   const int q = blockIdx.x;
-  const int ctx = a.q_start + q + 1;
+  const QRange rg = query_range(a.qpos, a.qfirst, a.q_start, a.L, q);
+  const int ctx = rg.hi - rg.lo + 1;
+  if (ctx <= 0) {  // empty context: nothing passes, nothing is needed (uniform)
+    if (tid == 0) a.tau[q] = __builtin_inff();
+    return;
+  }
   const int mq = min(a.M, ctx);
   const int64_t num = (int64_t)a.oversample * a.topk * mq;
   int r = (int)((num + ctx - 1) / ctx);
@@ -200,7 +205,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_tau_kernel(SampleArgs a
 
   for (int cb = wave; cb * 16 < mq; cb += kSampleThreads / kWave) {
     const int j = cb * 16 + (lane & 15);
-    const int pos = j < mq ? (int)(((int64_t)j * ctx) / mq) : -1;
+    const int pos = j < mq ? rg.lo + (int)(((int64_t)j * ctx) / mq) : -1;
     Frag b[KS];
     const uint8_t* row = a.k + (int64_t)(pos >= 0 ? pos : 0) * RBYTES;
 #pragma unroll
@@ -226,14 +231,19 @@ __global__ void __launch_bounds__(kSampleThreads) sample_tau_kernel(SampleArgs a
         }
       }
     }
-    float s = 0.0f;
+    // The selection kernels' head-sum order (as in replay_kernel): a lane's
+    // partial over its heads, then lane ^ 32 (the other row-block parity of
+    // the pair tile), then lane ^ 16 (the other half).  A sampled key's score
+    // is then bit-identical to the score the fused kernel compares with tau,
+    // so the r sampled keys at or above tau always pass.
+    float p = 0.0f;
 #pragma unroll
     for (int rb = 0; rb < RB4; ++rb) {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) s = __builtin_fmaf(__builtin_fmaxf(acc[rb][i], 0.0f), wf[rb][i], s);
+      for (int i = 0; i < 4; ++i) p = __builtin_fmaf(__builtin_fmaxf(acc[rb][i], 0.0f), wf[rb][i], p);
     }
-    s += __shfl_xor(s, 16);
-    s += __shfl_xor(s, 32);
+    const float t = p + __shfl_xor(p, 32);
+    float s = t + __shfl_xor(t, 16);
     if constexpr (FP8) s *= pos >= 0 ? a.k_scale[pos] : 0.0f;
     if (lane < 16 && j < mq) S[j] = s;
   }

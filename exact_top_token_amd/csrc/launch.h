@@ -26,6 +26,8 @@ struct ScoreArgs {
   uint2* cand;
   float* rows;
   const int* qlist;
+  const int* qpos;     // [n] query positions, or null (q_start + i)
+  const int* qfirst;   // [n] first key of each query's context, or null (0)
   int64_t row_stride;
   int L;
   int q_start;
@@ -48,6 +50,8 @@ struct SampleArgs {
   const float* q_scale;
   const float* k_scale;
   float* tau;
+  const int* qpos;
+  const int* qfirst;
   int L;
   int q_start;
   int n;
@@ -90,18 +94,19 @@ hipError_t launch_zero(int* cnt, int n, DevStats* st, hipStream_t s);
 
 // Check: flags queries whose candidate count is above cap or below
 // min(k, ctx) and appends them to `failed`.
-hipError_t launch_check(const int* cnt, int n, int q_start, int topk, int cap, DevStats* st,
-                        int* failed, hipStream_t s);
+hipError_t launch_check(const int* cnt, int n, const int* qpos, const int* qfirst, int q_start,
+                        int L, int topk, int cap, DevStats* st, int* failed, hipStream_t s);
 
 // Exact top-k of each passing query's candidates (failed queries are skipped).
-hipError_t launch_cand_select(const int* cnt, const uint2* cand, int n, int q_start, int topk,
-                              int cap, int L, int* out_idx, float* out_score, hipStream_t s);
+hipError_t launch_cand_select(const int* cnt, const uint2* cand, int n, const int* qpos,
+                              const int* qfirst, int q_start, int topk, int cap, int L,
+                              int* out_idx, float* out_score, hipStream_t s);
 
 // Exact top-k of score rows: entry e is row rows[e * row_stride] of query
 // qlist[e] (or q_offset + e).
 hipError_t launch_row_topk(const float* rows, int64_t row_stride, const int* qlist, int q_offset,
-                           int nq, int q_start, int topk, int L, int* out_idx, float* out_score,
-                           hipStream_t s);
+                           int nq, const int* qpos, const int* qfirst, int q_start, int topk, int L,
+                           int* out_idx, float* out_score, hipStream_t s);
 
 // LDS bytes cand_select needs for this cap / k (the host checks the limit).
 size_t cand_select_lds_bytes(int cap, int topk);

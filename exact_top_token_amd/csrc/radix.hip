@@ -141,13 +141,13 @@ hipError_t launch_zero(int* cnt, int n, DevStats* st, hipStream_t s) {
   return hipGetLastError();
 }
 
-__global__ void check_kernel(const int* cnt, int n, int q_start, int topk, int cap, DevStats* st,
-                             int* failed) {
+__global__ void check_kernel(const int* cnt, int n, const int* qpos, const int* qfirst, int q_start,
+                             int L, int topk, int cap, DevStats* st, int* failed) {
   const int i = blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n) return;
   const int c = cnt[i];
-  const int ctx = q_start + i + 1;
-  const int need = min(topk, ctx);
+  const QRange rg = query_range(qpos, qfirst, q_start, L, i);
+  const int need = min(topk, max(0, rg.hi - rg.lo + 1));
   const bool over = c > cap, under = c < need;
   atomicAdd(&st->cand_total, (unsigned long long)c);
   atomicMax(&st->cand_max, c);
@@ -156,10 +156,10 @@ __global__ void check_kernel(const int* cnt, int n, int q_start, int topk, int c
   if (over || under) failed[atomicAdd(&st->n_failed, 1)] = i;
 }
 
-hipError_t launch_check(const int* cnt, int n, int q_start, int topk, int cap, DevStats* st,
-                        int* failed, hipStream_t s) {
-  hipLaunchKernelGGL(check_kernel, dim3((n + 255) / 256), dim3(256), 0, s, cnt, n, q_start, topk,
-                     cap, st, failed);
+hipError_t launch_check(const int* cnt, int n, const int* qpos, const int* qfirst, int q_start,
+                        int L, int topk, int cap, DevStats* st, int* failed, hipStream_t s) {
+  hipLaunchKernelGGL(check_kernel, dim3((n + 255) / 256), dim3(256), 0, s, cnt, n, qpos, qfirst,
+                     q_start, L, topk, cap, st, failed);
   return hipGetLastError();
 }
 
@@ -216,16 +216,26 @@ size_t cand_select_lds_bytes(int cap, int topk) {
 // query's candidates span a narrow range, so the radix digits start at the
 // highest bit in which two candidate keys differ.
 __global__ void __launch_bounds__(kSelThreads) cand_select_kernel(const int* cnt, const uint2* cand,
-                                                                  int q_start, int topk, int cap,
-                                                                  int L, int* out_idx,
-                                                                  float* out_score) {
+                                                                  const int* qpos,
+                                                                  const int* qfirst, int q_start,
+                                                                  int topk, int cap, int L,
+                                                                  int* out_idx, float* out_score) {
   extern __shared__ uint32_t dyn[];
   __shared__ CandShared sh;
   const int q = blockIdx.x, tid = threadIdx.x, lane = tid & 63;
   const int c = cnt[q];
-  const int ctx = q_start + q + 1;
-  const int need = min(topk, ctx);
+  const QRange rg = query_range(qpos, qfirst, q_start, L, q);
+  const int need = min(topk, max(0, rg.hi - rg.lo + 1));
   if (c > cap || c < need) return;  // failed: recovered on the row path
+  int* oi = out_idx + (int64_t)q * topk;
+  float* os = out_score ? out_score + (int64_t)q * topk : nullptr;
+  if (need == 0) {  // empty context: all padding (uniform)
+    for (int i = tid; i < topk; i += kSelThreads) {
+      oi[i] = -1;
+      if (os) os[i] = -__builtin_inff();
+    }
+    return;
+  }
   uint32_t* ck = dyn;               // [cap] candidate score keys (later: sort scratch)
   uint32_t* sk = dyn + max(cap, 2 * topk);  // [topk] kept keys
   uint32_t* sp = sk + topk;         // [topk] kept positions
@@ -309,8 +319,6 @@ __global__ void __launch_bounds__(kSelThreads) cand_select_kernel(const int* cnt
       if (!sh.tie) break;  // uniform
     }
   }
-  int* oi = out_idx + (int64_t)q * topk;
-  float* os = out_score ? out_score + (int64_t)q * topk : nullptr;
   for (int i = tid; i < topk; i += kSelThreads) {
     if (i < need) {
       oi[i] = (int)rp[i];
@@ -322,14 +330,15 @@ __global__ void __launch_bounds__(kSelThreads) cand_select_kernel(const int* cnt
   }
 }
 
-hipError_t launch_cand_select(const int* cnt, const uint2* cand, int n, int q_start, int topk,
-                              int cap, int L, int* out_idx, float* out_score, hipStream_t s) {
+hipError_t launch_cand_select(const int* cnt, const uint2* cand, int n, const int* qpos,
+                              const int* qfirst, int q_start, int topk, int cap, int L,
+                              int* out_idx, float* out_score, hipStream_t s) {
   const size_t lds = cand_select_lds_bytes(cap, topk);
   hipError_t e = hipFuncSetAttribute((const void*)cand_select_kernel,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(cand_select_kernel, dim3((unsigned)n), dim3(kSelThreads), lds, s, cnt, cand,
-                     q_start, topk, cap, L, out_idx, out_score);
+                     qpos, qfirst, q_start, topk, cap, L, out_idx, out_score);
   return hipGetLastError();
 }
 
@@ -346,14 +355,24 @@ struct RowShared {
 
 __global__ void __launch_bounds__(kSelThreads) row_topk_kernel(const float* rows, int64_t row_stride,
                                                                const int* qlist, int q_offset,
+                                                               const int* qpos, const int* qfirst,
                                                                int q_start, int topk, int L,
                                                                int* out_idx, float* out_score) {
   __shared__ RowShared sh;
   const int e = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int q = qlist ? qlist[e] : q_offset + e;
-  const int ctx = q_start + q + 1;
+  const QRange rg = query_range(qpos, qfirst, q_start, L, q);
+  const int ctx = max(0, rg.hi - rg.lo + 1);
   const int need = min(topk, ctx);
-  const float* row = rows + (int64_t)e * row_stride;
+  if (need == 0) {  // empty context: all padding (uniform)
+    for (int i = tid; i < topk; i += kSelThreads) {
+      out_idx[(int64_t)q * topk + i] = -1;
+      if (out_score) out_score[(int64_t)q * topk + i] = -__builtin_inff();
+    }
+    return;
+  }
+  // the row holds the scores of keys lo..hi at their key positions
+  const float* row = rows + (int64_t)e * row_stride + rg.lo;
   int rem, mult;
   const uint32_t v = block_select_largest(
       ctx, need, [&](int i) { return score_key(row[i]); }, [](int) { return true; }, sh.rs, rem,
@@ -391,7 +410,7 @@ __global__ void __launch_bounds__(kSelThreads) row_topk_kernel(const float* rows
       const int slot = out + __popcll(mk & lt);
       if (slot < need) {  // exactly `need` entries qualify; the guard keeps LDS writes in bounds
         sh.sk[0][slot] = kk;
-        sh.sp[0][slot] = (uint32_t)i;
+        sh.sp[0][slot] = (uint32_t)(rg.lo + i);
       }
     }
     out += __popcll(mk);
@@ -404,11 +423,12 @@ __global__ void __launch_bounds__(kSelThreads) row_topk_kernel(const float* rows
 }
 
 hipError_t launch_row_topk(const float* rows, int64_t row_stride, const int* qlist, int q_offset,
-                           int nq, int q_start, int topk, int L, int* out_idx, float* out_score,
-                           hipStream_t s) {
+                           int nq, const int* qpos, const int* qfirst, int q_start, int topk, int L,
+                           int* out_idx, float* out_score, hipStream_t s) {
   if (nq <= 0) return hipSuccess;
   hipLaunchKernelGGL(row_topk_kernel, dim3((unsigned)nq), dim3(kSelThreads), 0, s, rows,
-                     row_stride, qlist, q_offset, q_start, topk, L, out_idx, out_score);
+                     row_stride, qlist, q_offset, qpos, qfirst, q_start, topk, L, out_idx,
+                     out_score);
   return hipGetLastError();
 }
 

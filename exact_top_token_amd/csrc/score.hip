@@ -50,6 +50,7 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t t3[TILE_BYTES];
   __shared__ uint2 stage[ROWS ? 1 : 8][2][kSB];
   __shared__ int s_maxt[8];
+  __shared__ int s_minlo[8];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4;
   const int group = blockIdx.x / a.nsplit, split = blockIdx.x % a.nsplit;
@@ -59,18 +60,27 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
   const int qa = ea < 0 ? -1 : (a.qlist ? a.qlist[ea] : a.q_offset + ea);
   const int qb = eb < 0 ? -1 : (a.qlist ? a.qlist[eb] : a.q_offset + eb);
 
+  // Key ranges of the pair (an absent or empty query gets lo > hi).
+  const QRange ra = qa >= 0 ? query_range(a.qpos, a.qfirst, a.q_start, a.L, qa) : QRange{1, 0};
+  const QRange rb = qb >= 0 ? query_range(a.qpos, a.qfirst, a.q_start, a.L, qb) : QRange{1, 0};
   if (lane == 0) {
-    int m = -1;
-    if (qa >= 0) m = a.q_start + qa;
-    if (qb >= 0) m = max(m, a.q_start + qb);
+    int m = -1, lo = 0x7fffffff;
+    if (ra.lo <= ra.hi) { m = ra.hi; lo = ra.lo; }
+    if (rb.lo <= rb.hi) { m = max(m, rb.hi); lo = min(lo, rb.lo); }
     s_maxt[wave] = m;
+    s_minlo[wave] = lo;
   }
   __syncthreads();
-  int maxt = s_maxt[0];
+  int maxt = s_maxt[0], minlo = s_minlo[0];
 #pragma unroll
-  for (int w = 1; w < 8; ++w) maxt = max(maxt, s_maxt[w]);
-  const int kb = split * a.split_len;
-  const int ke = min(kb + a.split_len, maxt + 1);
+  for (int w = 1; w < 8; ++w) {
+    maxt = max(maxt, s_maxt[w]);
+    minlo = min(minlo, s_minlo[w]);
+  }
+  // This split's keys that some query of the group sees, from a tile
+  // boundary: [kb, ke).
+  const int kb = max(split * a.split_len, minlo & ~(kTK - 1));
+  const int ke = min(split * a.split_len + a.split_len, maxt + 1);
   if (kb >= ke) return;  // uniform over the workgroup
   const int ntiles = (ke - kb + kTK - 1) / kTK;
 
@@ -103,7 +113,9 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
   const int sel = lane >> 5;
   const int qs = sel ? qb : qa;
   const int es = sel ? eb : ea;
-  const int lim = qs >= 0 ? min(a.q_start + qs + 1, ke) : 0;
+  const QRange rs = sel ? rb : ra;
+  const int first = rs.lo;                    // keys first .. lim - 1 of this split
+  const int lim = qs >= 0 ? min(rs.hi + 1, ke) : 0;
   float tau = 0.0f;
   if (!ROWS) tau = qs >= 0 ? a.tau[qs] : 0.0f;
   const bool owner = (lane & 16) == 0;  // lanes 0..15 and 32..47 own distinct (query, key)
@@ -155,7 +167,7 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         const int key = k0 + cb * 16 + (lane & 15);
-        if (owner && key < lim) a.rows[(int64_t)es * a.row_stride + key] = sc[cb];
+        if (owner && key >= first && key < lim) a.rows[(int64_t)es * a.row_stride + key] = sc[cb];
       }
     } else {
       // One uniform branch per tile: the candidate path runs only when some
@@ -164,13 +176,13 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
         const int key = k0 + cb * 16 + (lane & 15);
-        any |= owner && key < lim && sc[cb] >= tau;
+        any |= owner && key >= first && key < lim && sc[cb] >= tau;
       }
       if (__ballot(any)) {
 #pragma unroll
         for (int cb = 0; cb < NCB; ++cb) {
           const int key = k0 + cb * 16 + (lane & 15);
-          const bool pass = owner && key < lim && sc[cb] >= tau;
+          const bool pass = owner && key >= first && key < lim && sc[cb] >= tau;
           const uint64_t m = __ballot(pass);
           if (m) {
             const uint32_t mA = (uint32_t)(m & 0xFFFFull);

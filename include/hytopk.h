@@ -73,14 +73,26 @@ typedef enum {
   HYTOPK_PATH_ROWS_ALL = 1  /* skip the threshold: score every row, then row top-k (the full rescore) */
 } hytopk_path;
 
+/* Problem shape.  By default query i sits at position q_start + i and sees
+ * keys 0 .. q_start + i (one causal block at the end of the key buffer).
+ * The two optional device arrays generalise that: q_pos[i] gives query i's
+ * position (queries in any order, e.g. a context-parallel zigzag shard) and
+ * q_first[i] the first key of its context (several sequences packed back to
+ * back in one key buffer); query i then sees keys q_first[i] .. q_pos[i].
+ * Values are clamped to [0, L); a query whose range is empty gets only
+ * padding.  The sample count M is taken from L, the keys of the call; the
+ * sample positions and the threshold rank from the query's own context.
+ * Replay and backward take explicit indices and ignore both arrays. */
 typedef struct {
   int64_t L;        /* number of keys */
   int64_t n;        /* number of queries */
-  int64_t q_start;  /* position of query 0; query i has position q_start + i */
+  int64_t q_start;  /* position of query 0 when q_pos is NULL (q_start + n <= L) */
   int32_t H;        /* indexer heads */
   int32_t d;        /* head dimension */
   int32_t k;        /* keys kept per query */
   int32_t dtype;    /* hytopk_dtype of q and k */
+  const int32_t* q_pos;    /* optional [n] device: query positions; NULL = q_start + i */
+  const int32_t* q_first;  /* optional [n] device: first key of each context; NULL = 0 */
 } hytopk_problem;
 
 /* Sampled-threshold parameters.  Zero selects the default shown.

@@ -59,12 +59,16 @@ def assert_exact(inp, queries, idx_gpu: np.ndarray, score_gpu: np.ndarray, ref_i
         assert np.all(np.isneginf(score_gpu[r][~ok])), f"query {i} padding"
 
 
-def assert_structure(t: int, k: int, idx: np.ndarray, score: np.ndarray, where: str):
-    ctx = t + 1
+def assert_structure(t: int, k: int, idx: np.ndarray, score: np.ndarray, where: str,
+                     first: int = 0):
+    """Structure of one output row; the query sees keys first..t."""
+    ctx = max(0, t - first + 1)
     m = min(k, ctx)
     kept = idx[:m]
     assert np.all(idx[m:] == -1) and np.all(np.isneginf(score[m:])), f"{where}: padding"
-    assert kept.min() >= 0 and kept.max() <= t, f"{where}: index out of range"
+    if m == 0:
+        return
+    assert kept.min() >= first and kept.max() <= t, f"{where}: index out of range"
     assert np.unique(kept).size == m, f"{where}: duplicate indices"
     sc = score[:m]
     assert np.all(np.diff(sc) <= 0), f"{where}: scores not non-increasing"
@@ -73,10 +77,12 @@ def assert_structure(t: int, k: int, idx: np.ndarray, score: np.ndarray, where: 
 
 
 def assert_float_row(t: int, k: int, row: np.ndarray, idx: np.ndarray, score: np.ndarray,
-                     where: str, replay: np.ndarray | None = None):
-    assert_structure(t, k, idx, score, where)
-    m = min(k, t + 1)
-    kept = idx[:m].astype(np.int64)
+                     where: str, replay: np.ndarray | None = None, first: int = 0):
+    """Float comparators for one query seeing keys first..t; ``row`` is the
+    oracle's score row over that context (entry j = key first + j)."""
+    assert_structure(t, k, idx, score, where, first)
+    m = min(k, t - first + 1)
+    kept = idx[:m].astype(np.int64) - first
     ref = row[kept]
     err = np.abs(score[:m].astype(np.float64) - ref)
     assert np.all(err <= REL * (np.abs(ref) + 1.0)), f"{where}: score error {err.max():.3g}"
