@@ -18,6 +18,8 @@ tiny        4,096      256    4   64   256    q,k ints U{-3..3} (bf16), w ints U
 mid         131,072    2,048  64  128  2,048  q,k ~ N(0,1)/sqrt(d) bf16, w ~ U(0,1)/H
 glm1m       1,048,576  8,192  64  128  2,048  as mid
 glm1m_fp8   1,048,576  8,192  64  128  2,048  glm1m's fp32 draws, per-token E4M3
+glm1m_mxfp8 1,048,576  8,192  64  128  2,048  glm1m's fp32 draws, MX: E4M3 + E8M0 / 32
+glm1m_mxfp4 1,048,576  8,192  64  128  2,048  glm1m's fp32 draws, MX: E2M1 + E8M0 / 32
 stress_a    1,048,576  8,192  64  128  2,048  clustered keys + planted failures
 stress_b    1,048,576  8,192  64  128  2,048  clustered keys + >64 planted failures
 ==========  =========  =====  ==  ===  =====  =====================================
@@ -41,7 +43,7 @@ import numpy as np
 
 __all__ = [
     "CONFIGS", "Inputs", "make", "make_custom", "make_packed", "f32_to_bf16_bits",
-    "f32_to_e4m3", "quantize_e4m3_per_row", "subset_queries",
+    "f32_to_e4m3", "f32_to_e2m1", "quantize_e4m3_per_row", "quantize_mx", "subset_queries",
 ]
 
 CONFIGS = {
@@ -49,6 +51,8 @@ CONFIGS = {
     "mid": dict(L=131072, n=2048, H=64, d=128, k=2048, dtype="bf16", dist="normal", seed=1002),
     "glm1m": dict(L=1048576, n=8192, H=64, d=128, k=2048, dtype="bf16", dist="normal", seed=1003),
     "glm1m_fp8": dict(L=1048576, n=8192, H=64, d=128, k=2048, dtype="fp8", dist="normal", seed=1003),
+    "glm1m_mxfp8": dict(L=1048576, n=8192, H=64, d=128, k=2048, dtype="mxfp8", dist="normal", seed=1003),
+    "glm1m_mxfp4": dict(L=1048576, n=8192, H=64, d=128, k=2048, dtype="mxfp4", dist="normal", seed=1003),
 }
 STRESS_NAMES = ("stress_a", "stress_b")   # built by datagen.stress
 
@@ -59,7 +63,10 @@ class Inputs:
 
     ``q`` is ``[n][H][d]`` and ``k`` is ``[L][d]``: uint16 bf16 bit patterns, or
     uint8 OCP E4M3 codes when ``dtype == "fp8"`` (then ``q_scale[n]`` and
-    ``k_scale[L]`` are the fp32 per-token dequantisation scales).  ``w`` is
+    ``k_scale[L]`` are the fp32 per-token dequantisation scales).  For the MX
+    formats ``dtype == "mxfp8"`` / ``"mxfp4"`` the codes are E4M3 bytes or
+    E2M1 nibbles packed two per byte (last axis d / 2), and ``q_scale``
+    ``[n][H][d/32]`` / ``k_scale`` ``[L][d/32]`` hold E8M0 block scales.  ``w`` is
     ``[n][H]`` fp32.  Query ``i`` sits at position ``q_start + i`` and sees
     keys ``0 ..`` that position, unless ``q_pos`` / ``q_first`` (int32 ``[n]``)
     give its position and the first key of its context explicitly.
@@ -99,7 +106,7 @@ def f32_to_e4m3(x: np.ndarray) -> np.ndarray:
     a = np.minimum(np.abs(x), 448.0)
     f, E = np.frexp(a)                      # a = f * 2^E, f in [0.5, 1)
     e = E.astype(np.int64) - 1              # a = (2f) * 2^e, 2f in [1, 2)
-    normal = e >= -6
+    normal = (e >= -6) & (a > 0)            # zero takes the subnormal branch
     m = np.rint((2.0 * f - 1.0) * 8.0).astype(np.int64)   # ties to even
     carry = m == 8
     e = np.where(carry, e + 1, e)
@@ -124,6 +131,57 @@ def quantize_e4m3_per_row(x32: np.ndarray) -> tuple[np.ndarray, np.ndarray]:
         b = min(rows.shape[0], a + step)
         codes[a:b] = f32_to_e4m3(rows[a:b].astype(np.float64) / scale[a:b, None].astype(np.float64))
     return codes.reshape(x32.shape), scale
+
+
+# OCP Microscaling (MX) formats: blocks of 32 consecutive elements along the
+# head dimension share one E8M0 scale 2^(e - 127).  The block scale follows
+# the format's recipe: shared exponent = floor(log2(amax)) - emax, where emax
+# is the exponent of the element format's largest normal value (E4M3: 448 =
+# 1.75 * 2^8, emax 8; E2M1: 6 = 1.5 * 2^2, emax 2); elements are x / 2^shared
+# rounded to nearest (ties to even) and saturated.
+MX_BLOCK = 32
+_MX_EMAX = {"mxfp8": 8, "mxfp4": 2}
+
+
+def f32_to_e2m1(x: np.ndarray) -> np.ndarray:
+    """Encode values to E2M1 codes (0..15: sign bit 3, magnitudes 0, 0.5, 1,
+    1.5, 2, 3, 4, 6 for codes 0..7), round to nearest, ties to even code,
+    saturating to 6."""
+    x = np.asarray(x, dtype=np.float64)
+    a = np.minimum(np.abs(x), 6.0)
+    code = np.where(a < 2.0, np.rint(2.0 * a),
+                    np.where(a < 4.0, np.rint(a) + 2.0, np.rint(a / 2.0) + 4.0)).astype(np.int64)
+    sign = np.where(np.signbit(x), 8, 0)
+    return (code | sign).astype(np.uint8)
+
+
+def quantize_mx(x32: np.ndarray, fmt: str) -> tuple[np.ndarray, np.ndarray]:
+    """MX quantisation along the last axis (a multiple of 32).  Returns
+    (codes, scales): E4M3 bytes (same shape) or E2M1 codes packed two per byte
+    (element 2i in the low nibble of byte i; last axis halved), and the E8M0
+    scale bytes [..., last / 32]."""
+    x = np.asarray(x32, dtype=np.float32)
+    shp = x.shape
+    if shp[-1] % MX_BLOCK:
+        raise ValueError("the last axis must be a multiple of 32")
+    nb = shp[-1] // MX_BLOCK
+    flat = x.reshape(-1, nb, MX_BLOCK)
+    codes = np.empty(flat.shape, dtype=np.uint8)
+    scales = np.empty(flat.shape[:2], dtype=np.uint8)
+    step = max(1, (1 << 22) // (nb * MX_BLOCK))
+    for a in range(0, flat.shape[0], step):
+        blk = flat[a:a + step].astype(np.float64)
+        amax = np.abs(blk).max(axis=2)
+        with np.errstate(divide="ignore"):
+            e = np.where(amax > 0, np.floor(np.log2(np.where(amax > 0, amax, 1.0))) - _MX_EMAX[fmt], -127)
+        e = np.clip(e, -127, 127).astype(np.int64)
+        scales[a:a + step] = (e + 127).astype(np.uint8)
+        v = blk / np.exp2(e.astype(np.float64))[:, :, None]
+        codes[a:a + step] = f32_to_e4m3(v) if fmt == "mxfp8" else f32_to_e2m1(v)
+    codes = codes.reshape(shp)
+    if fmt == "mxfp4":
+        codes = (codes[..., 0::2] | (codes[..., 1::2] << 4)).astype(np.uint8)
+    return codes, scales.reshape(shp[:-1] + (nb,))
 
 
 def _draw(cfg: dict, rng: np.random.Generator):
@@ -155,6 +213,10 @@ def make_custom(name: str, L: int, n: int, H: int, d: int, k: int, dtype: str = 
     if dtype == "fp8":
         qc, qs = quantize_e4m3_per_row(q32)
         kc, ks = quantize_e4m3_per_row(k32)
+        return Inputs(name, L, n, H, d, k, dtype, qc, kc, w, qs, ks)
+    if dtype in ("mxfp8", "mxfp4"):
+        qc, qs = quantize_mx(q32, dtype)
+        kc, ks = quantize_mx(k32, dtype)
         return Inputs(name, L, n, H, d, k, dtype, qc, kc, w, qs, ks)
     raise ValueError(dtype)
 
@@ -196,6 +258,10 @@ def make_packed(name: str, seq_lens, chunks, H: int, d: int, k: int, dtype: str 
     elif dtype == "fp8":
         qc, qs = quantize_e4m3_per_row(q32)
         kc, ks = quantize_e4m3_per_row(k32)
+        inp = Inputs(name, L, n, H, d, k, dtype, qc, kc, w, qs, ks)
+    elif dtype in ("mxfp8", "mxfp4"):
+        qc, qs = quantize_mx(q32, dtype)
+        kc, ks = quantize_mx(k32, dtype)
         inp = Inputs(name, L, n, H, d, k, dtype, qc, kc, w, qs, ks)
     else:
         raise ValueError(dtype)

@@ -24,7 +24,8 @@ exactly that result [Abstract: HyTopK finds each query's exact top-k without a
 score table]:
 
 1. decode the stored inputs exactly to fp64 (bf16 bits; OCP E4M3 codes times
-   their per-token fp32 scales; fp32 head weights);
+   their per-token fp32 scales; OCP MX block-scaled E4M3 / E2M1 elements times
+   their E8M0 scale per 32 elements; fp32 head weights);
 2. score every causal pair (query position t sees keys 0..t; with packed
    sequences, the keys from its own sequence's first key through t) with the
    learned-sparse-attention indexer I(t,s) = sum_h w[t,h] * ReLU(q[t,h] . k[s]).
@@ -91,6 +92,41 @@ def decode_e4m3(codes: np.ndarray) -> np.ndarray:
     return np.where((c & 0x7F) == 0x7F, np.nan, out)
 
 
+def decode_e2m1(codes: np.ndarray) -> np.ndarray:
+    """OCP FP4 E2M1 codes (0..15) -> fp64, from the format: 1 sign bit, 2
+    exponent bits (bias 1), 1 mantissa bit; exponent 0 is subnormal (m/2);
+    no infinity or NaN, largest value 1.5 * 2^2 = 6."""
+    c = np.asarray(codes, dtype=np.uint8).astype(np.int64) & 0xF
+    sign = np.where((c >> 3) & 1, -1.0, 1.0)
+    e = (c >> 1) & 0x3
+    m = (c & 0x1).astype(np.float64)
+    normal = sign * (1.0 + m / 2.0) * np.exp2(e.astype(np.float64) - 1.0)
+    return np.where(e == 0, sign * m / 2.0, normal)
+
+
+def decode_e8m0(b: np.ndarray) -> np.ndarray:
+    """OCP E8M0 scale bytes -> fp64: 2^(b - 127); 0xFF is NaN."""
+    x = np.asarray(b, dtype=np.uint8).astype(np.float64)
+    return np.where(x == 255, np.nan, np.exp2(x - 127.0))
+
+
+def decode_mx(codes: np.ndarray, scales: np.ndarray, fmt: str) -> np.ndarray:
+    """MX block-scaled values -> fp64: every 32 consecutive elements of the
+    last axis share one E8M0 scale.  ``mxfp8``: E4M3 bytes; ``mxfp4``: E2M1
+    codes two per byte, element 2i in the low nibble of byte i."""
+    c = np.asarray(codes, dtype=np.uint8)
+    if fmt == "mxfp8":
+        v = _e4m3_lookup(c)
+    elif fmt == "mxfp4":
+        v = np.empty(c.shape[:-1] + (2 * c.shape[-1],), dtype=np.float64)
+        v[..., 0::2] = decode_e2m1(c & 0xF)
+        v[..., 1::2] = decode_e2m1(c >> 4)
+    else:
+        raise ValueError(fmt)
+    sc = np.repeat(decode_e8m0(scales), 32, axis=-1)
+    return v * sc
+
+
 _BF16_TABLE = None
 _E4M3_TABLE = None
 
@@ -125,6 +161,8 @@ class Decoded:
         elif inp.dtype == "fp8":
             self.keys = _e4m3_lookup(inp.k_)
             self.keys *= inp.k_scale.astype(np.float64)[:, None]
+        elif inp.dtype in ("mxfp8", "mxfp4"):
+            self.keys = decode_mx(inp.k_, inp.k_scale, inp.dtype)
         else:
             raise ValueError(inp.dtype)
 
@@ -133,8 +171,10 @@ class Decoded:
         inp = self.inp
         if inp.dtype == "bf16":
             q = _bf16_lookup(inp.q[i])
-        else:
+        elif inp.dtype == "fp8":
             q = _e4m3_lookup(inp.q[i]) * float(inp.q_scale[i])
+        else:
+            q = decode_mx(inp.q[i], inp.q_scale[i], inp.dtype)
         return q, inp.w[i].astype(np.float64)
 
     def position(self, i: int) -> int:

@@ -113,6 +113,7 @@ def test_datagen_encoders_round_to_nearest_even():
     ref = torch.from_numpy(x).to(torch.bfloat16).view(torch.int16).numpy().view(np.uint16)
     assert np.array_equal(datagen.f32_to_bf16_bits(x), ref)
     y = np.clip(rng.standard_normal(200000) * 40, -448, 448)
+    y[:6] = [0.0, -0.0, 2.0 ** -10, -(2.0 ** -10), 2.0 ** -9, 3.0]  # zeros, subnormals
     ref8 = torch.from_numpy(y).to(torch.float8_e4m3fn).view(torch.uint8).numpy()
     assert np.array_equal(datagen.f32_to_e4m3(y), ref8)
     assert datagen.f32_to_e4m3(np.array([1e6, -1e6]))[0] == 0x7E  # saturates
