@@ -14,11 +14,12 @@ import os
 __all__ = [
     "Problem", "Params", "Stats", "load_library", "library_path", "select", "replay",
     "baseline_select", "select_workspace_bytes", "baseline_workspace_bytes", "HytopkError",
-    "EXPORTS", "BF16", "FP8_E4M3", "PATH_AUTO", "PATH_ROWS_ALL", "trace_enable", "trace_read",
+    "EXPORTS", "BF16", "FP8_E4M3", "MXFP8_E4M3", "MXFP4_E2M1", "PATH_AUTO", "PATH_ROWS_ALL", "trace_enable", "trace_read",
     "backward", "backward_workspace_bytes",
 ]
 
-BF16, FP8_E4M3 = 0, 1
+BF16, FP8_E4M3, MXFP8_E4M3, MXFP4_E2M1 = 0, 1, 2, 3
+_FMT = {"bf16": BF16, "fp8": FP8_E4M3, "mxfp8": MXFP8_E4M3, "mxfp4": MXFP4_E2M1}
 PATH_AUTO, PATH_ROWS_ALL = 0, 1
 EXPORTS = (
     "hytopk_select_workspace", "hytopk_baseline_workspace", "hytopk_select", "hytopk_replay",
@@ -117,8 +118,12 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
-def _dtype_code(q) -> int:
+def _dtype_code(q, fmt=None) -> int:
+    """Storage format: ``fmt`` ("bf16", "fp8", "mxfp8", "mxfp4") when given,
+    else bf16 or per-token FP8 from the tensor dtype."""
     import torch
+    if fmt is not None:
+        return _FMT[fmt]
     if q.dtype == torch.bfloat16:
         return BF16
     if q.dtype in (torch.float8_e4m3fn, torch.uint8):
@@ -126,11 +131,14 @@ def _dtype_code(q) -> int:
     raise TypeError(f"q/k must be bfloat16 or float8_e4m3fn, got {q.dtype}")
 
 
-def _problem(q, k, w, topk: int, q_start, q_pos=None, q_first=None) -> Problem:
+def _problem(q, k, w, topk: int, q_start, q_pos=None, q_first=None, fmt=None) -> Problem:
+    """q [n][H][d] and k [L][d] (MXFP4: the last axis holds d/2 bytes)."""
     import torch
-    n, H, d = q.shape
+    code = _dtype_code(q, fmt)
+    n, H, dq = q.shape
+    d = 2 * dq if code == MXFP4_E2M1 else dq
     L = k.shape[0]
-    if k.shape[1] != d or tuple(w.shape) != (n, H):
+    if k.shape[1] != dq or tuple(w.shape) != (n, H):
         raise ValueError("shapes must be q [n][H][d], k [L][d], w [n][H]")
     for t in (q, k, w):
         if not t.is_cuda or not t.is_contiguous():
@@ -141,7 +149,7 @@ def _problem(q, k, w, topk: int, q_start, q_pos=None, q_first=None) -> Problem:
             raise ValueError("q_pos / q_first must be contiguous int32 [n] tensors on the GPU")
     if q_start is None:
         q_start = 0 if q_pos is not None else L - n
-    return Problem(L, n, int(q_start), H, d, int(topk), _dtype_code(q),
+    return Problem(L, n, int(q_start), H, d, int(topk), code,
                    None if q_pos is None else q_pos.data_ptr(),
                    None if q_first is None else q_first.data_ptr())
 
@@ -181,9 +189,9 @@ def trace_read() -> dict:
 
 
 def select_workspace_bytes(q, k, w, topk: int, q_start=None, params=None, q_pos=None,
-                           q_first=None) -> int:
+                           q_first=None, fmt=None) -> int:
     lib = load_library()
-    prob = _problem(q, k, w, topk, q_start, q_pos, q_first)
+    prob = _problem(q, k, w, topk, q_start, q_pos, q_first, fmt)
     prm = _params(params)
     return int(lib.hytopk_select_workspace(ctypes.byref(prob), ctypes.byref(prm) if prm else None))
 
@@ -194,14 +202,16 @@ def baseline_workspace_bytes(q, k, w, topk: int, q_start=None) -> int:
 
 
 def select(q, k, w, topk: int, *, q_scale=None, k_scale=None, q_start=None, params=None,
-           workspace=None, out=None, with_stats: bool = False, q_pos=None, q_first=None):
+           workspace=None, out=None, with_stats: bool = False, q_pos=None, q_first=None,
+           fmt=None):
     """Exact top-k per query (HyTopK).  Returns (idx int32 [n][k], score fp32
     [n][k]) and, with ``with_stats``, a dict of what the call did.  q_pos /
     q_first (int32 [n] on the GPU, optional) give each query's position and
-    the first key of its context (packed sequences)."""
+    the first key of its context (packed sequences).  ``fmt`` selects the MX
+    formats ("mxfp8", "mxfp4"; q_scale / k_scale then hold E8M0 bytes)."""
     import torch
     lib = load_library()
-    prob = _problem(q, k, w, topk, q_start, q_pos, q_first)
+    prob = _problem(q, k, w, topk, q_start, q_pos, q_first, fmt)
     prm = _params(params)
     need = int(lib.hytopk_select_workspace(ctypes.byref(prob), ctypes.byref(prm) if prm else None))
     if need == 0:
@@ -230,11 +240,11 @@ def select(q, k, w, topk: int, *, q_scale=None, k_scale=None, q_start=None, para
     return idx, score, d
 
 
-def replay(q, k, w, idx, *, q_scale=None, k_scale=None, q_start=None, out=None):
+def replay(q, k, w, idx, *, q_scale=None, k_scale=None, q_start=None, out=None, fmt=None):
     """Selection replay: scores of the saved indices idx [n][k] (-inf at idx < 0)."""
     import torch
     lib = load_library()
-    prob = _problem(q, k, w, idx.shape[1], q_start)
+    prob = _problem(q, k, w, idx.shape[1], q_start, fmt=fmt)
     if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.shape[0] != prob.n:
         raise ValueError("idx must be a contiguous int32 [n][k] tensor")
     if out is None:
@@ -245,11 +255,11 @@ def replay(q, k, w, idx, *, q_scale=None, k_scale=None, q_start=None, out=None):
 
 
 def baseline_select(q, k, w, topk: int, *, q_scale=None, k_scale=None, q_start=None,
-                    workspace=None, out=None, q_pos=None, q_first=None):
+                    workspace=None, out=None, q_pos=None, q_first=None, fmt=None):
     """The materialise-then-top-k route (writes the n x L fp32 score table)."""
     import torch
     lib = load_library()
-    prob = _problem(q, k, w, topk, q_start, q_pos, q_first)
+    prob = _problem(q, k, w, topk, q_start, q_pos, q_first, fmt)
     need = int(lib.hytopk_baseline_workspace(ctypes.byref(prob)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)

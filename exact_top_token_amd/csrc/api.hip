@@ -111,8 +111,9 @@ int check_problem(const hytopk_problem* p) {
   if (p->H > 64) return fail(HYTOPK_EUNSUPPORTED, "H > 64");
   if (p->dtype == HYTOPK_BF16) {
     if (p->d != 64 && p->d != 128) return fail(HYTOPK_EUNSUPPORTED, "bf16 needs d in {64, 128}");
-  } else if (p->dtype == HYTOPK_FP8_E4M3) {
-    if (p->d != 128) return fail(HYTOPK_EUNSUPPORTED, "fp8 needs d = 128");
+  } else if (p->dtype == HYTOPK_FP8_E4M3 || p->dtype == HYTOPK_MXFP8_E4M3 ||
+             p->dtype == HYTOPK_MXFP4_E2M1) {
+    if (p->d != 128) return fail(HYTOPK_EUNSUPPORTED, "fp8 and MX formats need d = 128");
   } else {
     return fail(HYTOPK_EINVAL, "unknown dtype");
   }
@@ -179,11 +180,11 @@ int check_ws(void* ws, size_t bytes, size_t need) {
   return HYTOPK_OK;
 }
 
-int check_inputs(const hytopk_problem* p, const void* q, const float* qs, const void* k,
-                 const float* ks, const float* w) {
+int check_inputs(const hytopk_problem* p, const void* q, const void* qs, const void* k,
+                 const void* ks, const float* w) {
   if (!q || !k || !w) return fail(HYTOPK_EINVAL, "q, k and w must be non-NULL");
-  if (p->dtype == HYTOPK_FP8_E4M3 && (!qs || !ks))
-    return fail(HYTOPK_EINVAL, "fp8 needs q_scale and k_scale");
+  if (p->dtype != HYTOPK_BF16 && (!qs || !ks))
+    return fail(HYTOPK_EINVAL, "fp8 and MX formats need q_scale and k_scale");
   return HYTOPK_OK;
 }
 
@@ -224,8 +225,8 @@ BwdLayout bwd_layout(const hytopk_problem* p) {
   return l;
 }
 
-hk::ScoreArgs score_args(const hytopk_problem* p, const void* q, const float* qs, const void* k,
-                         const float* ks, const float* w) {
+hk::ScoreArgs score_args(const hytopk_problem* p, const void* q, const void* qs, const void* k,
+                         const void* ks, const float* w) {
   hk::ScoreArgs a{};
   a.q = static_cast<const uint8_t*>(q);
   a.k = static_cast<const uint8_t*>(k);
@@ -256,10 +257,9 @@ int rows_path(const hytopk_problem* p, const hk::ScoreArgs& base, const int* qli
   a.q_offset = q_offset;
   a.nq = nq;
   splits(nq, maxctx, a.nsplit, a.split_len);
-  const bool fp8 = p->dtype == HYTOPK_FP8_E4M3;
   {
     Span sp("score_rows", s);
-    HK_HIP(hk::launch_score(a, p->d, fp8, s), "score rows launch");
+    HK_HIP(hk::launch_score(a, p->d, p->dtype, s), "score rows launch");
   }
   {
     Span sp("row_topk", s);
@@ -338,7 +338,7 @@ size_t hytopk_baseline_workspace(const hytopk_problem* p) {
 }
 
 int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void* q,
-                  const float* q_scale, const void* k, const float* k_scale, const float* w,
+                  const void* q_scale, const void* k, const void* k_scale, const float* w,
                   int32_t* out_idx, float* out_score, void* workspace, size_t workspace_bytes,
                   void* stream, hytopk_stats* stats) {
   g_err.clear();
@@ -359,7 +359,7 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
   hk::DevStats* dst = reinterpret_cast<hk::DevStats*>(ws + l.stats);
   uint2* cand = reinterpret_cast<uint2*>(ws + l.cand);
   float* rows = reinterpret_cast<float*>(ws + l.rows);
-  const bool fp8 = p->dtype == HYTOPK_FP8_E4M3;
+  const int fmt = p->dtype;
   const int n = (int)p->n;
   const int64_t maxctx = ctx_bound(p, p->n);
   const hk::ScoreArgs base = score_args(p, q, q_scale, k, k_scale, w);
@@ -375,7 +375,7 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
     sa.topk = p->k; sa.M = sample_count(p, r); sa.oversample = r.oversample;
     {
       Span sp("sample_tau", s);
-      HK_HIP(hk::launch_sample_tau(sa, p->d, fp8, s), "sample/threshold launch");
+      HK_HIP(hk::launch_sample_tau(sa, p->d, fmt, s), "sample/threshold launch");
     }
 
     hk::ScoreArgs a = base;
@@ -387,7 +387,7 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
     splits(n, maxctx, a.nsplit, a.split_len);
     {
       Span sp("score_compact", s);
-      HK_HIP(hk::launch_score(a, p->d, fp8, s), "fused score launch");
+      HK_HIP(hk::launch_score(a, p->d, fmt, s), "fused score launch");
     }
     {
       Span sp("check", s);
@@ -443,8 +443,8 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
   return HYTOPK_OK;
 }
 
-int hytopk_replay(const hytopk_problem* p, const void* q, const float* q_scale, const void* k,
-                  const float* k_scale, const float* w, const int32_t* idx, float* out_score,
+int hytopk_replay(const hytopk_problem* p, const void* q, const void* q_scale, const void* k,
+                  const void* k_scale, const float* w, const int32_t* idx, float* out_score,
                   void* stream) {
   g_err.clear();
   int rc = check_problem(p);
@@ -465,12 +465,12 @@ int hytopk_replay(const hytopk_problem* p, const void* q, const float* q_scale, 
   a.topk = p->k;
   hipStream_t s = static_cast<hipStream_t>(stream);
   Span sp("replay", s);
-  HK_HIP(hk::launch_replay(a, p->d, p->dtype == HYTOPK_FP8_E4M3, s), "replay launch");
+  HK_HIP(hk::launch_replay(a, p->d, p->dtype, s), "replay launch");
   return HYTOPK_OK;
 }
 
-int hytopk_baseline_select(const hytopk_problem* p, const void* q, const float* q_scale,
-                           const void* k, const float* k_scale, const float* w, int32_t* out_idx,
+int hytopk_baseline_select(const hytopk_problem* p, const void* q, const void* q_scale,
+                           const void* k, const void* k_scale, const float* w, int32_t* out_idx,
                            float* out_score, void* workspace, size_t workspace_bytes,
                            void* stream) {
   g_err.clear();
@@ -491,8 +491,8 @@ size_t hytopk_backward_workspace(const hytopk_problem* p) {
   return bwd_layout(p).total;
 }
 
-int hytopk_backward(const hytopk_problem* p, const void* q, const float* q_scale, const void* k,
-                    const float* k_scale, const float* w, const int32_t* idx,
+int hytopk_backward(const hytopk_problem* p, const void* q, const void* q_scale, const void* k,
+                    const void* k_scale, const float* w, const int32_t* idx,
                     const float* d_score, float* dq, float* dw, float* dk, void* workspace,
                     size_t workspace_bytes, void* stream) {
   g_err.clear();

@@ -4,6 +4,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 namespace hk {
 
 constexpr int kWave = 64;
@@ -12,6 +14,75 @@ typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef int i32x8 __attribute__((ext_vector_type(8)));
 typedef unsigned u32x4 __attribute__((ext_vector_type(4)));
+
+// Storage formats of q and k (the values of hytopk_dtype).
+constexpr int kBF16 = 0;   // bf16
+constexpr int kFP8 = 1;    // OCP FP8 E4M3 with fp32 per-token scales
+constexpr int kMXFP8 = 2;  // OCP MX: E4M3 elements, one E8M0 scale per 32
+constexpr int kMXFP4 = 3;  // OCP MX: E2M1 elements (two per byte), E8M0 per 32
+
+// Per-format constants of the 16x16 MFMA tiles.  bf16 uses
+// v_mfma_f32_16x16x32_bf16 (K = 32, 8 elements = 16 bytes per lane per
+// k-step); the other formats use v_mfma_scale_f32_16x16x128_f8f6f4 (K = 128,
+// 32 elements per lane per k-step: 32 bytes of E4M3 or 16 bytes of E2M1, the
+// latter in the low four registers of the operand).  The scaled MFMA takes
+// one E8M0 scale per lane for A and one for B: the scale of the lane's row
+// (A) or column (B) over its 32 elements -- exactly one MX block.
+template <int FMT>
+struct Fmt {
+  static constexpr bool SCALED = FMT != kBF16;                 // f8f6f4 MFMA
+  static constexpr bool MX = FMT == kMXFP8 || FMT == kMXFP4;   // block scales
+  static constexpr int BITS = FMT == kBF16 ? 16 : (FMT == kMXFP4 ? 4 : 8);
+  static constexpr int KMMA = FMT == kBF16 ? 32 : 128;         // K per MFMA
+  static constexpr int FB = FMT == kBF16 ? 16 : (FMT == kMXFP4 ? 16 : 32);
+  static constexpr int CODE = FMT == kMXFP4 ? 4 : 0;           // f8f6f4 operand format
+  using Frag = typename std::conditional<FMT == kBF16, bf16x8, i32x8>::type;
+
+  // D += A x B with per-lane E8M0 scales sa, sb (127 = 2^0; ignored for bf16).
+  __device__ __forceinline__ static f32x4 mma(const Frag& a, const Frag& b, const f32x4& c, int sa,
+                                              int sb) {
+    if constexpr (FMT == kBF16) {
+      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
+    } else {
+      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, CODE, CODE, 0, sa, 0, sb);
+    }
+  }
+
+  // Bytes of one k-step slice of a row (KMMA elements).
+  static constexpr int SLICE = KMMA * BITS / 8;
+
+  // 16-byte chunks of a k-step slice that lane group g holds, in operand
+  // order (chunk c = bytes [16c, 16c + 16) of the slice).  bf16 and E2M1
+  // hold one chunk, g.  Per-token E4M3 holds the contiguous chunks 2g and
+  // 2g + 1 (any layout shared by A and B gives the same sums).  Under MX
+  // block scales E4M3 must follow the instruction's K order: the operand's
+  // first 16 bytes are K = 16g .. 16g + 15 and its last 16 bytes K = 64 + 16g
+  // .. 64 + 16g + 15, and lane group b's scale applies to K = 32b .. 32b + 31,
+  // so lane group g holds chunks g and 4 + g (measured on gfx950 with
+  // single-element operands).
+  __device__ __forceinline__ static int chunk0(int g) {
+    return FMT == kFP8 ? 2 * g : g;
+  }
+  __device__ __forceinline__ static int chunk1(int g) {
+    return FMT == kFP8 ? 2 * g + 1 : 4 + g;
+  }
+
+  // Lane group g's fragment of the k-step slice starting at `slice`
+  // (E2M1 fragments fill the low four registers).
+  __device__ __forceinline__ static Frag frag(const uint8_t* slice, int g) {
+    if constexpr (FMT == kBF16) {
+      return *reinterpret_cast<const Frag*>(slice + 16 * g);
+    } else if constexpr (FMT == kMXFP4) {
+      const u32x4 v = *reinterpret_cast<const u32x4*>(slice + 16 * g);
+      return i32x8{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+    } else {
+      const u32x4 lo = *reinterpret_cast<const u32x4*>(slice + 16 * chunk0(g));
+      const u32x4 hi = *reinterpret_cast<const u32x4*>(slice + 16 * chunk1(g));
+      return i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
+                   (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
+  }
+};
 
 // Order-preserving 32-bit key of an fp32 score: larger score <=> larger key.
 // -0.0 is folded onto +0.0 so that equal scores always have equal keys.

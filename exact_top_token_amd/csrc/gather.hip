@@ -19,56 +19,111 @@ namespace hk {
 constexpr int kReplayThreads = 256;  // 4 waves, one query each
 constexpr int kReplayDepth = 3;      // column blocks of keys in flight per wave
 
-// One query per wave.  Row block rb holds heads 16 rb .. 16 rb + 15, so lane
-// group g holds heads 16 rb + 4 g + i: exactly the heads that half (g & 1) of
-// the pair tile holds in its row blocks of parity (g >> 1).  Each lane forms
-// the same partial sum the pair tile forms for that half and parity, then the
-// partials are combined in the pair tile's order ((even + odd), then the
-// other half), which makes every replayed score bit-identical to the selected
-// one.  The keys of a column block are the query's own, so no MFMA work is
-// wasted, and kReplayDepth column blocks of gathers are kept in flight.
-template <int RB4, int D, bool FP8>
-__global__ void __launch_bounds__(kReplayThreads) replay_kernel(ReplayArgs a) {
-  constexpr int ESIZE = FP8 ? 1 : 2;
-  constexpr int RBYTES = D * ESIZE;
-  constexpr int FB = FP8 ? 32 : 16;
-  constexpr int KS = RBYTES / (4 * FB);
-  using Frag = typename std::conditional<FP8, i32x8, bf16x8>::type;
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4;
-  const int q = blockIdx.x * (kReplayThreads / kWave) + wave;
-  if (q >= a.n) return;  // wave-uniform; no workgroup barrier in this kernel
-  const int K = a.topk;
+// One query per wave, RB4 row blocks of 16 heads against 16 keys: the tile
+// shared by replay and the sampled threshold.  Row block rb holds heads
+// 16 rb .. 16 rb + 15, so lane group g holds heads 16 rb + 4 g + i: exactly
+// the heads that half (g & 1) of the pair tile holds in its row blocks of
+// parity (g >> 1).  Each lane forms the same partial sum the pair tile forms
+// for that half and parity, then the partials are combined in the pair
+// tile's order ((even + odd), then the other half), which makes every score
+// bit-identical to the one the selection kernels compute.
+template <int RB4, int D, int FMT>
+struct QueryTile {
+  using F = Fmt<FMT>;
+  using Frag = typename F::Frag;
+  static constexpr int RBYTES = D * F::BITS / 8;
+  static constexpr int FB = F::FB;
+  static constexpr int KS = D / F::KMMA;
+  static constexpr int NBLK = D / 32;
+  static_assert(KS >= 1 && D % F::KMMA == 0, "unsupported head dimension");
 
   Frag qa[RB4][KS];
+  int sa[RB4][KS];
   float wf[RB4][4];
-  {
-    const int r = lane & 15;
-    const float qs = FP8 ? a.q_scale[q] : 1.0f;
+
+  __device__ __forceinline__ void load(const uint8_t* q, const float* w, const void* q_scale, int H,
+                                       int qi) {
+    const int lane = lane_id(), r = lane & 15, g = lane >> 4;
+    float qs = 1.0f;
+    if constexpr (FMT == kFP8) qs = static_cast<const float*>(q_scale)[qi];
 #pragma unroll
     for (int rb = 0; rb < RB4; ++rb) {
       const int h = 16 * rb + r;
-      const uint8_t* src = a.q + ((int64_t)q * a.H + (h < a.H ? h : 0)) * RBYTES;
+      const int64_t hr = (int64_t)qi * H + (h < H ? h : 0);
+      const uint8_t* src = q + hr * RBYTES;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if (h < a.H) {
-          qa[rb][ks] = *reinterpret_cast<const Frag*>(src + (4 * ks + g) * FB);
-        } else {
-          qa[rb][ks] = Frag{};
+        qa[rb][ks] = h < H ? F::frag(src + ks * F::SLICE, g) : Frag{};
+        sa[rb][ks] = 127;
+        if constexpr (F::MX) {
+          if (h < H) sa[rb][ks] = static_cast<const uint8_t*>(q_scale)[hr * NBLK + 4 * ks + g];
         }
       }
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int hw = 16 * rb + 4 * g + i;
-        wf[rb][i] = hw < a.H ? a.w[(int64_t)q * a.H + hw] * qs : 0.0f;
+        wf[rb][i] = hw < H ? w[(int64_t)qi * H + hw] * qs : 0.0f;
       }
     }
   }
+
+  // The lane's fragments of key row `key` (-1: zeros) and their MX scales.
+  __device__ __forceinline__ static void key(const uint8_t* k, const void* k_scale, int key,
+                                             Frag (&b)[KS], int (&sb)[KS]) {
+    const int g = lane_id() >> 4;
+    const uint8_t* row = k + (int64_t)(key >= 0 ? key : 0) * RBYTES;
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+      b[ks] = key >= 0 ? F::frag(row + ks * F::SLICE, g) : Frag{};
+      sb[ks] = 127;
+      if constexpr (F::MX) {
+        if (key >= 0) sb[ks] = static_cast<const uint8_t*>(k_scale)[(int64_t)key * NBLK + 4 * ks + g];
+      }
+    }
+  }
+
+  // Score of (query, key lane % 16), in every lane, before the FP8 key scale.
+  __device__ __forceinline__ float score(const Frag (&b)[KS], const int (&sb)[KS]) const {
+    f32x4 acc[RB4];
+#pragma unroll
+    for (int rb = 0; rb < RB4; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) {
+#pragma unroll
+      for (int rb = 0; rb < RB4; ++rb) acc[rb] = F::mma(qa[rb][ks], b[ks], acc[rb], sa[rb][ks], sb[ks]);
+    }
+    float p = 0.0f;
+#pragma unroll
+    for (int rb = 0; rb < RB4; ++rb) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p = __builtin_fmaf(__builtin_fmaxf(acc[rb][i], 0.0f), wf[rb][i], p);
+    }
+    const float t = p + __shfl_xor(p, 32);  // even + odd row blocks of this half
+    return t + __shfl_xor(t, 16);           // + the other half
+  }
+};
+
+// Replay: each 16-key column block holds the query's own indices, so no MFMA
+// work is wasted; kReplayDepth column blocks of gathers are kept in flight.
+template <int RB4, int D, int FMT>
+__global__ void __launch_bounds__(kReplayThreads) replay_kernel(ReplayArgs a) {
+  using T = QueryTile<RB4, D, FMT>;
+  using Frag = typename T::Frag;
+  constexpr int KS = T::KS;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int q = blockIdx.x * (kReplayThreads / kWave) + wave;
+  if (q >= a.n) return;  // wave-uniform; no workgroup barrier in this kernel
+  const int K = a.topk;
+
+  T qt;
+  qt.load(a.q, a.w, a.q_scale, a.H, q);
 
   const int* ids = a.idx + (int64_t)q * K;
   float* out = a.out + (int64_t)q * K;
   const int nblk = (K + 15) / 16;
 
   Frag buf[kReplayDepth][KS];
+  int sbuf[kReplayDepth][KS];
   int kid[kReplayDepth];
   float ksc[kReplayDepth];
   auto fetch = [&](int blk, int slot) {
@@ -76,16 +131,8 @@ __global__ void __launch_bounds__(kReplayThreads) replay_kernel(ReplayArgs a) {
     int key = (blk < nblk && j < K) ? ids[j] : -1;
     if (key >= a.L) key = -1;  // out-of-range indices are padding, never dereferenced
     kid[slot] = key;
-    const uint8_t* row = a.k + (int64_t)(key >= 0 ? key : 0) * RBYTES;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (key >= 0) {
-        buf[slot][ks] = *reinterpret_cast<const Frag*>(row + (4 * ks + g) * FB);
-      } else {
-        buf[slot][ks] = Frag{};
-      }
-    }
-    if constexpr (FP8) ksc[slot] = key >= 0 ? a.k_scale[key] : 0.0f;
+    T::key(a.k, a.k_scale, key, buf[slot], sbuf[slot]);
+    if constexpr (FMT == kFP8) ksc[slot] = key >= 0 ? static_cast<const float*>(a.k_scale)[key] : 0.0f;
   };
 #pragma unroll
   for (int d = 0; d < kReplayDepth - 1; ++d) fetch(d, d);
@@ -96,54 +143,40 @@ __global__ void __launch_bounds__(kReplayThreads) replay_kernel(ReplayArgs a) {
       const int b = blk + d;
       if (b >= nblk) break;  // wave-uniform
       fetch(b + kReplayDepth - 1, (d + kReplayDepth - 1) % kReplayDepth);
-      f32x4 acc[RB4];
-#pragma unroll
-      for (int rb = 0; rb < RB4; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-        for (int rb = 0; rb < RB4; ++rb) {
-          if constexpr (FP8) {
-            acc[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[rb][ks], buf[d][ks], acc[rb],
-                                                                        0, 0, 0, 127, 0, 127);
-          } else {
-            acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rb][ks], buf[d][ks], acc[rb], 0, 0, 0);
-          }
-        }
-      }
-      float p = 0.0f;
-#pragma unroll
-      for (int rb = 0; rb < RB4; ++rb) {
-#pragma unroll
-        for (int i = 0; i < 4; ++i) p = __builtin_fmaf(__builtin_fmaxf(acc[rb][i], 0.0f), wf[rb][i], p);
-      }
-      const float t = p + __shfl_xor(p, 32);   // even + odd row blocks of this half
-      float s = t + __shfl_xor(t, 16);         // + the other half
-      if constexpr (FP8) s *= ksc[d];
+      float s = qt.score(buf[d], sbuf[d]);
+      if constexpr (FMT == kFP8) s *= ksc[d];
       const int j = b * 16 + lane;
       if (lane < 16 && j < K) out[j] = kid[d] >= 0 ? s : -__builtin_inff();
     }
   }
 }
 
-template <int RB4, int D, bool FP8>
+template <int RB4, int D, int FMT>
 static hipError_t replay_rb(const ReplayArgs& a, hipStream_t s) {
   constexpr int per = kReplayThreads / kWave;
   dim3 grid((unsigned)((a.n + per - 1) / per)), block(kReplayThreads);
-  hipLaunchKernelGGL((replay_kernel<RB4, D, FP8>), grid, block, 0, s, a);
+  hipLaunchKernelGGL((replay_kernel<RB4, D, FMT>), grid, block, 0, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_replay(const ReplayArgs& a, int d, bool fp8, hipStream_t s) {
+template <int FMT>
+static hipError_t replay_d128(const ReplayArgs& a, bool small, hipStream_t s) {
+  return small ? replay_rb<1, 128, FMT>(a, s) : replay_rb<4, 128, FMT>(a, s);
+}
+
+hipError_t launch_replay(const ReplayArgs& a, int d, int fmt, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   // row blocks of 16 heads: 1 for the narrow pair tile (H <= 8), else 4
   const bool small = a.H <= 8;
-  if (fp8) {
-    if (d != 128) return hipErrorInvalidValue;
-    return small ? replay_rb<1, 128, true>(a, s) : replay_rb<4, 128, true>(a, s);
+  if (fmt == kBF16) {
+    if (d == 64) return small ? replay_rb<1, 64, kBF16>(a, s) : replay_rb<4, 64, kBF16>(a, s);
+    if (d == 128) return replay_d128<kBF16>(a, small, s);
+    return hipErrorInvalidValue;
   }
-  if (d == 64) return small ? replay_rb<1, 64, false>(a, s) : replay_rb<4, 64, false>(a, s);
-  if (d == 128) return small ? replay_rb<1, 128, false>(a, s) : replay_rb<4, 128, false>(a, s);
+  if (d != 128) return hipErrorInvalidValue;
+  if (fmt == kFP8) return replay_d128<kFP8>(a, small, s);
+  if (fmt == kMXFP8) return replay_d128<kMXFP8>(a, small, s);
+  if (fmt == kMXFP4) return replay_d128<kMXFP4>(a, small, s);
   return hipErrorInvalidValue;
 }
 
@@ -154,17 +187,15 @@ constexpr int kSampleThreads = 256;  // 4 waves share one query's samples
 // One query per workgroup.  Row block rb of the A operand holds heads
 // 16 rb .. 16 rb + 15 of the query; output lane group g holds heads
 // 16 rb + 4 g + i, summed in-lane, then across the four lane groups.
-template <int RB4, int D, bool FP8>
+template <int RB4, int D, int FMT>
 __global__ void __launch_bounds__(kSampleThreads) sample_tau_kernel(SampleArgs a) {
-  constexpr int ESIZE = FP8 ? 1 : 2;
-  constexpr int RBYTES = D * ESIZE;
-  constexpr int FB = FP8 ? 32 : 16;
-  constexpr int KS = RBYTES / (4 * FB);
-  using Frag = typename std::conditional<FP8, i32x8, bf16x8>::type;
+  using T = QueryTile<RB4, D, FMT>;
+  using Frag = typename T::Frag;
+  constexpr int KS = T::KS;
   extern __shared__ float S[];  // sample scores, M_q entries
   __shared__ RadixScratch sc;
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4;
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const int q = blockIdx.x;
   const QRange rg = query_range(a.qpos, a.qfirst, a.q_start, a.L, q);
   const int ctx = rg.hi - rg.lo + 1;
@@ -177,74 +208,20 @@ __global__ void __launch_bounds__(kSampleThreads) sample_tau_kernel(SampleArgs a
   int r = (int)((num + ctx - 1) / ctx);
   r = max(1, min(mq, r));
 
-  Frag qa[RB4][KS];
-  float wf[RB4][4];
-  {
-    const int rr = lane & 15;
-    float qs = 1.0f;
-    if (FP8) qs = a.q_scale[q];
-#pragma unroll
-    for (int rb = 0; rb < RB4; ++rb) {
-      const int h = 16 * rb + rr;
-      const uint8_t* src = a.q + ((int64_t)q * a.H + (h < a.H ? h : 0)) * RBYTES;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        if (h < a.H) {
-          qa[rb][ks] = *reinterpret_cast<const Frag*>(src + (4 * ks + g) * FB);
-        } else {
-          qa[rb][ks] = Frag{};
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int hw = 16 * rb + 4 * g + i;
-        wf[rb][i] = hw < a.H ? a.w[(int64_t)q * a.H + hw] * qs : 0.0f;
-      }
-    }
-  }
+  T qt;
+  qt.load(a.q, a.w, a.q_scale, a.H, q);
 
   for (int cb = wave; cb * 16 < mq; cb += kSampleThreads / kWave) {
     const int j = cb * 16 + (lane & 15);
     const int pos = j < mq ? rg.lo + (int)(((int64_t)j * ctx) / mq) : -1;
     Frag b[KS];
-    const uint8_t* row = a.k + (int64_t)(pos >= 0 ? pos : 0) * RBYTES;
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-      if (pos >= 0) {
-        b[ks] = *reinterpret_cast<const Frag*>(row + (4 * ks + g) * FB);
-      } else {
-        b[ks] = Frag{};
-      }
-    }
-    f32x4 acc[RB4];
-#pragma unroll
-    for (int rb = 0; rb < RB4; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int rb = 0; rb < RB4; ++rb) {
-        if constexpr (FP8) {
-          acc[rb] = __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(qa[rb][ks], b[ks], acc[rb], 0, 0,
-                                                                      0, 127, 0, 127);
-        } else {
-          acc[rb] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(qa[rb][ks], b[ks], acc[rb], 0, 0, 0);
-        }
-      }
-    }
-    // The selection kernels' head-sum order (as in replay_kernel): a lane's
-    // partial over its heads, then lane ^ 32 (the other row-block parity of
-    // the pair tile), then lane ^ 16 (the other half).  A sampled key's score
-    // is then bit-identical to the score the fused kernel compares with tau,
-    // so the r sampled keys at or above tau always pass.
-    float p = 0.0f;
-#pragma unroll
-    for (int rb = 0; rb < RB4; ++rb) {
-#pragma unroll
-      for (int i = 0; i < 4; ++i) p = __builtin_fmaf(__builtin_fmaxf(acc[rb][i], 0.0f), wf[rb][i], p);
-    }
-    const float t = p + __shfl_xor(p, 32);
-    float s = t + __shfl_xor(t, 16);
-    if constexpr (FP8) s *= pos >= 0 ? a.k_scale[pos] : 0.0f;
+    int sb[KS];
+    T::key(a.k, a.k_scale, pos, b, sb);
+    // The selection kernels' head-sum order: a sampled key's score is
+    // bit-identical to the score the fused kernel compares with tau, so the
+    // r sampled keys at or above tau always pass.
+    float s = qt.score(b, sb);
+    if constexpr (FMT == kFP8) s *= pos >= 0 ? static_cast<const float*>(a.k_scale)[pos] : 0.0f;
     if (lane < 16 && j < mq) S[j] = s;
   }
   __syncthreads();
@@ -254,27 +231,35 @@ __global__ void __launch_bounds__(kSampleThreads) sample_tau_kernel(SampleArgs a
   if (tid == 0) a.tau[q] = key_score(v);
 }
 
-template <int RB4, int D, bool FP8>
+template <int RB4, int D, int FMT>
 static hipError_t sample_rb(const SampleArgs& a, hipStream_t s) {
   const int mmax = a.M < a.L ? a.M : a.L;
   const size_t lds = (size_t)mmax * sizeof(float);
-  hipError_t e = hipFuncSetAttribute((const void*)sample_tau_kernel<RB4, D, FP8>,
+  hipError_t e = hipFuncSetAttribute((const void*)sample_tau_kernel<RB4, D, FMT>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)a.n), block(kSampleThreads);
-  hipLaunchKernelGGL((sample_tau_kernel<RB4, D, FP8>), grid, block, lds, s, a);
+  hipLaunchKernelGGL((sample_tau_kernel<RB4, D, FMT>), grid, block, lds, s, a);
   return hipGetLastError();
 }
 
-hipError_t launch_sample_tau(const SampleArgs& a, int d, bool fp8, hipStream_t s) {
+template <int FMT>
+static hipError_t sample_d128(const SampleArgs& a, bool small, hipStream_t s) {
+  return small ? sample_rb<1, 128, FMT>(a, s) : sample_rb<4, 128, FMT>(a, s);
+}
+
+hipError_t launch_sample_tau(const SampleArgs& a, int d, int fmt, hipStream_t s) {
   if (a.n <= 0) return hipSuccess;
   const bool small = a.H <= 16;
-  if (fp8) {
-    if (d != 128) return hipErrorInvalidValue;
-    return small ? sample_rb<1, 128, true>(a, s) : sample_rb<4, 128, true>(a, s);
+  if (fmt == kBF16) {
+    if (d == 64) return small ? sample_rb<1, 64, kBF16>(a, s) : sample_rb<4, 64, kBF16>(a, s);
+    if (d == 128) return sample_d128<kBF16>(a, small, s);
+    return hipErrorInvalidValue;
   }
-  if (d == 64) return small ? sample_rb<1, 64, false>(a, s) : sample_rb<4, 64, false>(a, s);
-  if (d == 128) return small ? sample_rb<1, 128, false>(a, s) : sample_rb<4, 128, false>(a, s);
+  if (d != 128) return hipErrorInvalidValue;
+  if (fmt == kFP8) return sample_d128<kFP8>(a, small, s);
+  if (fmt == kMXFP8) return sample_d128<kMXFP8>(a, small, s);
+  if (fmt == kMXFP4) return sample_d128<kMXFP4>(a, small, s);
   return hipErrorInvalidValue;
 }
 

@@ -19,8 +19,8 @@ struct ScoreArgs {
   const uint8_t* q;
   const uint8_t* k;
   const float* w;
-  const float* q_scale;
-  const float* k_scale;
+  const void* q_scale;   // fp32 [n] (FP8) or E8M0 [n][H][d/32] (MX)
+  const void* k_scale;   // fp32 [L] (FP8) or E8M0 [L][d/32] (MX)
   const float* tau;
   int* cnt;
   uint2* cand;
@@ -39,7 +39,7 @@ struct ScoreArgs {
   int split_len;
 };
 
-hipError_t launch_score(const ScoreArgs& a, int d, bool fp8, hipStream_t s);
+hipError_t launch_score(const ScoreArgs& a, int d, int fmt, hipStream_t s);
 
 // Per-query sampled threshold: tau[q] = the r-th largest of the M_q sample
 // scores at positions floor(j * ctx / M_q).
@@ -47,8 +47,8 @@ struct SampleArgs {
   const uint8_t* q;
   const uint8_t* k;
   const float* w;
-  const float* q_scale;
-  const float* k_scale;
+  const void* q_scale;   // fp32 [n] (FP8) or E8M0 [n][H][d/32] (MX)
+  const void* k_scale;   // fp32 [L] (FP8) or E8M0 [L][d/32] (MX)
   float* tau;
   const int* qpos;
   const int* qfirst;
@@ -61,15 +61,15 @@ struct SampleArgs {
   int oversample;
 };
 
-hipError_t launch_sample_tau(const SampleArgs& a, int d, bool fp8, hipStream_t s);
+hipError_t launch_sample_tau(const SampleArgs& a, int d, int fmt, hipStream_t s);
 
 // Replay: out[q][j] = I(q_start + q, idx[q][j]) (-inf where idx is outside [0, L)).
 struct ReplayArgs {
   const uint8_t* q;
   const uint8_t* k;
   const float* w;
-  const float* q_scale;
-  const float* k_scale;
+  const void* q_scale;   // fp32 [n] (FP8) or E8M0 [n][H][d/32] (MX)
+  const void* k_scale;   // fp32 [L] (FP8) or E8M0 [L][d/32] (MX)
   const int* idx;
   float* out;
   int L;
@@ -78,7 +78,7 @@ struct ReplayArgs {
   int topk;
 };
 
-hipError_t launch_replay(const ReplayArgs& a, int d, bool fp8, hipStream_t s);
+hipError_t launch_replay(const ReplayArgs& a, int d, int fmt, hipStream_t s);
 
 // Device counters of one selection call.
 struct DevStats {

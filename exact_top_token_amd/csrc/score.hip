@@ -33,15 +33,19 @@ constexpr int kSB = 128;         // staged candidates per query before a flush
 // (global_load_lds_dwordx4), three tiles ahead of the one being scored, with
 // one workgroup barrier per tile.  The stages are distinct LDS objects so the
 // compiler can tell the loads into one stage from reads of another.
-template <int RB, int D, bool FP8, bool ROWS>
+template <int RB, int D, int FMT, bool ROWS>
 __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
-  using T = PairTile<RB, D, FP8>;
+  using T = PairTile<RB, D, FMT>;
+  using F = Fmt<FMT>;
   using Frag = typename T::Frag;
   constexpr int RBYTES = T::RBYTES, NCH = T::NCH, KS = T::KS;
-  constexpr int TILE_BYTES = kTK * RBYTES;
+  // keys per stage: 64, or 128 for 64-byte E2M1 rows (every stage is 8-16 KB)
+  constexpr int TK = FMT == kMXFP4 ? 2 * kTK : kTK;
+  static_assert(!F::MX || KS == 1, "MX scales are loaded for one k-step");
+  constexpr int TILE_BYTES = TK * RBYTES;
   constexpr int OPS = TILE_BYTES / (kThreads * 16);  // 16-byte DMA loads per lane per tile
   constexpr int KPB = 1024 / RBYTES;                  // keys per 1 KB DMA block
-  constexpr int NCB = kTK / 16;                       // 16-key column blocks per tile
+  constexpr int NCB = TK / 16;                        // 16-key column blocks per tile
   static_assert(TILE_BYTES % (kThreads * 16) == 0, "tile must split evenly over the workgroup");
 
   __shared__ __attribute__((aligned(1024))) uint8_t t0[TILE_BYTES];
@@ -79,10 +83,10 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
   }
   // This split's keys that some query of the group sees, from a tile
   // boundary: [kb, ke).
-  const int kb = max(split * a.split_len, minlo & ~(kTK - 1));
+  const int kb = max(split * a.split_len, minlo & ~(TK - 1));
   const int ke = min(split * a.split_len + a.split_len, maxt + 1);
   if (kb >= ke) return;  // uniform over the workgroup
-  const int ntiles = (ke - kb + kTK - 1) / kTK;
+  const int ntiles = (ke - kb + TK - 1) / TK;
 
   // DMA layout: load p of wave w fills 1 KB block p * 8 + w of a stage; its
   // lane j lands on key kk = block * KPB + j / NCH, 16-byte slot j % NCH,
@@ -90,9 +94,9 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
   // fragment reads undo.  kk % NCH does not depend on p.
   const int dma_kk = wave * KPB + lane / NCH;
   const int dma_c = ((lane % NCH) ^ (dma_kk & (NCH - 1))) * 16;
-  const int full_tiles = (a.L - kb) / kTK;  // tiles that lie entirely below L
+  const int full_tiles = (a.L - kb) / TK;  // tiles that lie entirely below L
   auto issue = [&](int tile, uint8_t* buf) {
-    const int k0 = kb + tile * kTK;
+    const int k0 = kb + tile * TK;
     const uint8_t* base = a.k + (int64_t)k0 * RBYTES;
 #pragma unroll
     for (int p = 0; p < OPS; ++p) {
@@ -139,28 +143,39 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
     __builtin_amdgcn_wave_barrier();
   };
 
-  auto compute = [&](int it, const uint8_t* tb, const float (&ksc)[NCB]) {
-    const int k0 = kb + it * kTK;
+  // Per-key scales of a tile's column blocks: fp32 per token (FP8) or the
+  // E8M0 byte of the lane's block (MX).
+  struct KeyScales {
+    float f[NCB];
+    int e[NCB];
+  };
+  auto compute = [&](int it, const uint8_t* tb, const KeyScales& ksc) {
+    const int k0 = kb + it * TK;
     float sc[NCB];
 #pragma unroll
     for (int cb = 0; cb < NCB; ++cb) {
       const int kt = cb * 16 + (lane & 15);
       Frag b[KS];
+      int sb[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if constexpr (FP8) {
-          const int c0 = 2 * (4 * ks + g);
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(tb + kt * RBYTES + ((c0 ^ (kt & (NCH - 1))) * 16));
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(tb + kt * RBYTES + (((c0 + 1) ^ (kt & (NCH - 1))) * 16));
+        sb[ks] = F::MX ? ksc.e[cb] : 127;
+        // the chunks Fmt::frag names, at their swizzled places in the stage
+        constexpr int CPS = F::SLICE / 16;  // chunks per k-step slice
+        const uint8_t* krow = tb + kt * RBYTES;
+        if constexpr (F::FB == 32) {  // E4M3: two 16-byte chunks
+          const int c0 = CPS * ks + F::chunk0(g), c1 = CPS * ks + F::chunk1(g);
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(krow + ((c0 ^ (kt & (NCH - 1))) * 16));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(krow + ((c1 ^ (kt & (NCH - 1))) * 16));
           b[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
-        } else {
-          const int c = 4 * ks + g;
-          b[ks] = *reinterpret_cast<const Frag*>(tb + kt * RBYTES + ((c ^ (kt & (NCH - 1))) * 16));
+        } else {  // bf16 or E2M1: one 16-byte chunk (frag reads chunk g of its slice)
+          const int c = CPS * ks + g;
+          b[ks] = F::frag(krow + ((c ^ (kt & (NCH - 1))) * 16) - 16 * g, g);
         }
       }
-      float s = qt.score(b);
-      if constexpr (FP8) s *= ksc[cb];
+      float s = qt.score(b, sb);
+      if constexpr (FMT == kFP8) s *= ksc.f[cb];
       sc[cb] = s;
     }
     if constexpr (ROWS) {
@@ -205,23 +220,27 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
 
   // Per tile: wait for this wave's loads of tile `it`, barrier (every wave's
   // loads landed; every wave finished tile it-1), refill tile it-1's stage
-  // with tile it+3, score tile it.  FP8 key scales are read before the refill
+  // with tile it+3, score tile it.  Key scales are read before the refill
   // so that waiting for them never waits for the refill.
   auto step = [&](int it, const uint8_t* cur, uint8_t* refill) {
-    float ksc[NCB];
-    if constexpr (FP8) {
+    KeyScales ksc;
+    if constexpr (F::SCALED) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const int key = kb + it * kTK + cb * 16 + (lane & 15);
-        ksc[cb] = a.k_scale[min(key, a.L - 1)];
+        const int key = min(kb + it * TK + cb * 16 + (lane & 15), a.L - 1);
+        if constexpr (FMT == kFP8) {
+          ksc.f[cb] = static_cast<const float*>(a.k_scale)[key];
+        } else {
+          ksc.e[cb] = static_cast<const uint8_t*>(a.k_scale)[(int64_t)key * T::NBLK + g];
+        }
       }
     }
     if (it + 2 < ntiles) {
-      HK_WAIT_VM(2 * OPS + (FP8 ? NCB : 0));
+      HK_WAIT_VM(2 * OPS + (F::SCALED ? NCB : 0));
     } else if (it + 1 < ntiles) {
-      HK_WAIT_VM(OPS + (FP8 ? NCB : 0));
+      HK_WAIT_VM(OPS + (F::SCALED ? NCB : 0));
     } else {
-      HK_WAIT_VM(FP8 ? NCB : 0);
+      HK_WAIT_VM(F::SCALED ? NCB : 0);
     }
     __builtin_amdgcn_s_barrier();
     if (it + 3 < ntiles) issue(it + 3, refill);
@@ -239,27 +258,35 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
   }
 }
 
-template <int RB, int D, bool FP8>
+template <int RB, int D, int FMT>
 static hipError_t launch_rb(const ScoreArgs& a, hipStream_t s) {
   const int groups = (a.nq + 15) / 16;
   dim3 grid((unsigned)(groups * a.nsplit)), block(kThreads);
   if (a.rows) {
-    hipLaunchKernelGGL((score_tile_kernel<RB, D, FP8, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((score_tile_kernel<RB, D, FMT, true>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((score_tile_kernel<RB, D, FP8, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((score_tile_kernel<RB, D, FMT, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
 
-hipError_t launch_score(const ScoreArgs& a, int d, bool fp8, hipStream_t s) {
+template <int FMT>
+static hipError_t launch_d128(const ScoreArgs& a, bool small, hipStream_t s) {
+  return small ? launch_rb<1, 128, FMT>(a, s) : launch_rb<8, 128, FMT>(a, s);
+}
+
+hipError_t launch_score(const ScoreArgs& a, int d, int fmt, hipStream_t s) {
   if (a.nq <= 0) return hipSuccess;
   const bool small = a.H <= 8;
-  if (fp8) {
-    if (d != 128) return hipErrorInvalidValue;
-    return small ? launch_rb<1, 128, true>(a, s) : launch_rb<8, 128, true>(a, s);
+  if (fmt == kBF16) {
+    if (d == 64) return small ? launch_rb<1, 64, kBF16>(a, s) : launch_rb<8, 64, kBF16>(a, s);
+    if (d == 128) return launch_d128<kBF16>(a, small, s);
+    return hipErrorInvalidValue;
   }
-  if (d == 64) return small ? launch_rb<1, 64, false>(a, s) : launch_rb<8, 64, false>(a, s);
-  if (d == 128) return small ? launch_rb<1, 128, false>(a, s) : launch_rb<8, 128, false>(a, s);
+  if (d != 128) return hipErrorInvalidValue;
+  if (fmt == kFP8) return launch_d128<kFP8>(a, small, s);
+  if (fmt == kMXFP8) return launch_d128<kMXFP8>(a, small, s);
+  if (fmt == kMXFP4) return launch_d128<kMXFP4>(a, small, s);
   return hipErrorInvalidValue;
 }
 

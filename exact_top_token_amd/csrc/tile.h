@@ -1,16 +1,19 @@
 // The indexer tile: one wave scores a PAIR of queries against 16 keys at a
-// time with v_mfma_f32_16x16x32_bf16 (bf16) or v_mfma_scale_f32_16x16x128_f8f6f4
-// (OCP FP8 E4M3), then applies ReLU and the weighted head sum in registers.
+// time with 16x16 MFMAs (see Fmt in common.h for the per-format
+// instruction), then applies ReLU and the weighted head sum in registers.
 //
 // Indexer: I(t,s) = sum_h w[t,h] * ReLU(q[t,h] . k[s]).
 //
 // MFMA operand layout (16x16 output tile, 64 lanes, lane group g = lane / 16):
 //   A (16 rows x K): lane holds row (lane % 16); rows 0..7 are heads of query A
 //     and rows 8..15 heads of query B, so row block rb covers heads 8rb..8rb+7
-//     of both queries.  The K slice of lane group g at k-step ks is byte range
-//     [(4 ks + g) * FB, +FB) of the head's row (FB = 16 bytes for bf16,
-//     32 bytes for FP8); B uses the same slices, so every pair (row, key)
-//     meets the full d-dimension exactly once over the k-steps.
+//     of both queries.  Lane group g holds, at k-step ks, the chunks of the
+//     row's k-step slice that Fmt::frag names (one FB-byte run for bf16, E2M1
+//     and per-token E4M3); B uses the same chunks, so every pair (row, key)
+//     meets the full d-dimension exactly once over the k-steps.  For the MX
+//     formats lane group g's elements are the instruction's K block g, which
+//     is the row's 32-element block 4 ks + g, and the lane passes that
+//     block's E8M0 scale with its operand.
 //   B (K x 16 keys): lane holds key column (lane % 16).
 //   D: lane holds rows 4g..4g+3 of column (lane % 16): lanes 0..31 therefore
 //     hold 32 heads of query A (heads 8rb + 4(g & 1) + i), lanes 32..63 the
@@ -25,23 +28,26 @@
 
 namespace hk {
 
-template <int RB, int D, bool FP8>
+template <int RB, int D, int FMT>
 struct PairTile {
-  static constexpr int ESIZE = FP8 ? 1 : 2;              // bytes per element
-  static constexpr int RBYTES = D * ESIZE;                // bytes per head row / key row
-  static constexpr int FB = FP8 ? 32 : 16;                // fragment bytes per lane per k-step
-  static constexpr int KS = RBYTES / (4 * FB);            // k-steps over the d-dimension
+  using F = Fmt<FMT>;
+  using Frag = typename F::Frag;
+  static constexpr int RBYTES = D * F::BITS / 8;          // bytes per head row / key row
+  static constexpr int FB = F::FB;                        // fragment bytes per lane per k-step
+  static constexpr int KS = D / F::KMMA;                  // k-steps over the d-dimension
   static constexpr int NCH = RBYTES / 16;                 // 16-byte chunks per key row
+  static constexpr int NBLK = D / 32;                     // MX blocks per row
   static constexpr int HMAX = 8 * RB;                     // heads covered (zero-padded)
-  using Frag = typename std::conditional<FP8, i32x8, bf16x8>::type;
-  static_assert(KS >= 1 && RBYTES % (4 * FB) == 0, "unsupported head dimension");
+  static_assert(KS >= 1 && D % F::KMMA == 0, "unsupported head dimension");
 
   Frag a[RB][KS];   // query pair, A operand
+  int sa[RB][KS];   // E8M0 scale of each A fragment's block (MX; 127 otherwise)
   float wf[RB][4];  // head weights of this lane's 32 heads (times q_scale for FP8)
 
   // Load the A operand and weights of query indices qa / qb (-1 = absent).
+  // q_scale: fp32 [n] (FP8) or E8M0 bytes [n][H][D/32] (MX).
   __device__ __forceinline__ void load(const uint8_t* __restrict__ q, const float* __restrict__ w,
-                                       const float* __restrict__ q_scale, int H, int qa, int qb) {
+                                       const void* __restrict__ q_scale, int H, int qa, int qb) {
     const int lane = lane_id();
     const int r = lane & 15, g = lane >> 4;
     const int qrow = (r >> 3) ? qb : qa;
@@ -49,20 +55,23 @@ struct PairTile {
     for (int rb = 0; rb < RB; ++rb) {
       const int h = 8 * rb + (r & 7);
       const bool ok = qrow >= 0 && h < H;
-      const uint8_t* src = q + ((int64_t)(ok ? qrow : 0) * H + (ok ? h : 0)) * RBYTES;
+      const int64_t hr = (int64_t)(ok ? qrow : 0) * H + (ok ? h : 0);
+      const uint8_t* src = q + hr * RBYTES;
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        if (ok) {
-          a[rb][ks] = *reinterpret_cast<const Frag*>(src + (4 * ks + g) * FB);
-        } else {
-          a[rb][ks] = Frag{};
+        a[rb][ks] = ok ? F::frag(src + ks * F::SLICE, g) : Frag{};
+        sa[rb][ks] = 127;
+        if constexpr (F::MX) {
+          if (ok) sa[rb][ks] = static_cast<const uint8_t*>(q_scale)[hr * NBLK + 4 * ks + g];
         }
       }
     }
     const int qw = (lane >> 5) ? qb : qa;
     const int hb = 4 * (g & 1);
     float qs = 1.0f;
-    if (FP8 && qw >= 0) qs = q_scale[qw];
+    if constexpr (FMT == kFP8) {
+      if (qw >= 0) qs = static_cast<const float*>(q_scale)[qw];
+    }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
@@ -73,26 +82,17 @@ struct PairTile {
     }
   }
 
-  __device__ __forceinline__ static f32x4 mfma(const Frag& a, const Frag& b, const f32x4& c) {
-    if constexpr (FP8) {
-      // cbsz = blgp = 0: both operands OCP FP8 E4M3; scale exponents 127 = 2^0.
-      return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, 0, 0, 127, 0, 127);
-    } else {
-      return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
-    }
-  }
-
-  // Scores of both queries against 16 keys whose B fragments are b[ks].
-  // Returns this lane's score: query (lane < 32 ? A : B), key (lane % 16),
-  // before the per-key FP8 scale.
-  __device__ __forceinline__ float score(const Frag (&b)[KS]) const {
+  // Scores of both queries against 16 keys whose B fragments are b[ks] (with
+  // E8M0 scales sb[ks] for MX).  Returns this lane's score: query (lane < 32 ?
+  // A : B), key (lane % 16), before the per-key FP8 scale.
+  __device__ __forceinline__ float score(const Frag (&b)[KS], const int (&sb)[KS]) const {
     f32x4 acc[RB];
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int ks = 0; ks < KS; ++ks) {
 #pragma unroll
-      for (int rb = 0; rb < RB; ++rb) acc[rb] = mfma(a[rb][ks], b[ks], acc[rb]);
+      for (int rb = 0; rb < RB; ++rb) acc[rb] = F::mma(a[rb][ks], b[ks], acc[rb], sa[rb][ks], sb[ks]);
     }
     return epilogue(acc);
   }

@@ -26,10 +26,19 @@
  * Conventions for every entry point
  *   * All array arguments are DEVICE pointers to row-major, contiguous data on
  *     the current HIP device, except `stats`, which is a host pointer.
- *   * q is [n][H][d], k is [L][d]: bf16, or OCP FP8 E4M3 bytes (dtype
- *     HYTOPK_FP8_E4M3) with fp32 per-token dequantisation scales q_scale[n]
- *     and k_scale[L] (> 0; NULL for bf16).  w is [n][H] fp32.  Query i sits at
- *     position q_start + i and q_start + n <= L.
+ *   * q is [n][H][d], k is [L][d], in one of four storage formats (dtype):
+ *       HYTOPK_BF16        bf16; q_scale = k_scale = NULL;
+ *       HYTOPK_FP8_E4M3    OCP FP8 E4M3 bytes with fp32 per-token
+ *                          dequantisation scales q_scale[n], k_scale[L] (> 0);
+ *       HYTOPK_MXFP8_E4M3  OCP MX: E4M3 bytes, every 32 consecutive elements
+ *                          of a row share one E8M0 scale byte (2^(b - 127)):
+ *                          q_scale is uint8 [n][H][d/32], k_scale [L][d/32];
+ *       HYTOPK_MXFP4_E2M1  OCP MX: E2M1 elements packed two per byte (element
+ *                          2i in the low nibble of byte i, rows of d/2 bytes),
+ *                          E8M0 scales as for MXFP8.
+ *     The scale pointers are `const void*` for that reason.  w is [n][H]
+ *     fp32.  Query i sits at position q_start + i and q_start + n <= L unless
+ *     the problem's q_pos / q_first arrays say otherwise.
  *   * Index outputs are [n][k] int32, score outputs [n][k] fp32.  When a
  *     query's context ctx = q_start + i + 1 is shorter than k, the entries
  *     beyond ctx hold index -1 and score -inf.
@@ -44,7 +53,8 @@
  *     the calling thread's most recent failure.
  *   * Supported in this version: 1 <= H <= 64 (heads beyond a multiple of 8
  *     are zero-padded; H <= 8 uses a narrow tile); d in {64, 128} for bf16,
- *     d = 128 for FP8 E4M3; 1 <= k <= 2048; L < 2^31; cap <= 16384 and
+ *     d = 128 for FP8 E4M3 and the MX formats; the backward is bf16 only;
+ *     1 <= k <= 2048; L < 2^31; cap <= 16384 and
  *     m_max <= 16384.  Other shapes return HYTOPK_EUNSUPPORTED.
  */
 #ifndef HYTOPK_H_
@@ -65,7 +75,12 @@ typedef enum {
   HYTOPK_EHIP = -4           /* a HIP runtime call failed; see hytopk_last_error() */
 } hytopk_status;
 
-typedef enum { HYTOPK_BF16 = 0, HYTOPK_FP8_E4M3 = 1 } hytopk_dtype;
+typedef enum {
+  HYTOPK_BF16 = 0,
+  HYTOPK_FP8_E4M3 = 1,    /* per-token fp32 scales */
+  HYTOPK_MXFP8_E4M3 = 2,  /* OCP MX block scales, 32 elements per E8M0 scale */
+  HYTOPK_MXFP4_E2M1 = 3   /* OCP MX block scales, 32 elements per E8M0 scale */
+} hytopk_dtype;
 
 /* Path overrides for testing; results are identical on every path. */
 typedef enum {
@@ -141,7 +156,7 @@ size_t hytopk_baseline_workspace(const hytopk_problem* p);
  * out_idx [n][k] int32 receives positions; out_score [n][k] fp32 their scores
  * (may be NULL).  prm may be NULL (all defaults); stats may be NULL. */
 int hytopk_select(const hytopk_problem* p, const hytopk_params* prm,
-                  const void* q, const float* q_scale, const void* k, const float* k_scale,
+                  const void* q, const void* q_scale, const void* k, const void* k_scale,
                   const float* w, int32_t* out_idx, float* out_score,
                   void* workspace, size_t workspace_bytes, void* stream, hytopk_stats* stats);
 
@@ -151,15 +166,15 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm,
  * indices in (q_start + i, L) are scored although they lie after the query
  * (callers pass indices that selection returned).  The scores are
  * bit-identical to those hytopk_select returns for the same entries. */
-int hytopk_replay(const hytopk_problem* p, const void* q, const float* q_scale,
-                  const void* k, const float* k_scale, const float* w, const int32_t* idx,
+int hytopk_replay(const hytopk_problem* p, const void* q, const void* q_scale,
+                  const void* k, const void* k_scale, const float* w, const int32_t* idx,
                   float* out_score, void* stream);
 
 /* The conventional route: write the n x L fp32 score table into the
  * workspace, then a row top-k kernel reads it back.  Same outputs as
  * hytopk_select. */
-int hytopk_baseline_select(const hytopk_problem* p, const void* q, const float* q_scale,
-                           const void* k, const float* k_scale, const float* w,
+int hytopk_baseline_select(const hytopk_problem* p, const void* q, const void* q_scale,
+                           const void* k, const void* k_scale, const float* w,
                            int32_t* out_idx, float* out_score,
                            void* workspace, size_t workspace_bytes, void* stream);
 
@@ -185,8 +200,8 @@ size_t hytopk_backward_workspace(const hytopk_problem* p);
  * reproducible.  bf16 inputs only (HYTOPK_EUNSUPPORTED for fp8).  Products
  * use bf16 MFMA with every fp32 factor split into two bf16 parts (16
  * significant bits) and fp32 accumulation. */
-int hytopk_backward(const hytopk_problem* p, const void* q, const float* q_scale,
-                    const void* k, const float* k_scale, const float* w, const int32_t* idx,
+int hytopk_backward(const hytopk_problem* p, const void* q, const void* q_scale,
+                    const void* k, const void* k_scale, const float* w, const int32_t* idx,
                     const float* d_score, float* dq, float* dw, float* dk,
                     void* workspace, size_t workspace_bytes, void* stream);
 

@@ -33,13 +33,21 @@ def to_device(inp: datagen.Inputs, device: str = "cuda") -> dict:
         q = torch.from_numpy(inp.q.view(np.int16)).to(device).view(torch.bfloat16)
         k = torch.from_numpy(inp.k_.view(np.int16)).to(device).view(torch.bfloat16)
         qs = ks = None
-    else:
+    elif inp.dtype == "fp8":
         q = torch.from_numpy(inp.q).to(device).view(torch.float8_e4m3fn)
         k = torch.from_numpy(inp.k_).to(device).view(torch.float8_e4m3fn)
         qs = torch.from_numpy(inp.q_scale).to(device)
         ks = torch.from_numpy(inp.k_scale).to(device)
+    else:  # MX: raw code bytes and E8M0 scale bytes; the format goes as fmt=
+        q = torch.from_numpy(inp.q).to(device)
+        k = torch.from_numpy(inp.k_).to(device)
+        qs = torch.from_numpy(inp.q_scale).to(device)
+        ks = torch.from_numpy(inp.k_scale).to(device)
     w = torch.from_numpy(inp.w).to(device)
-    return dict(q=q, k=k, w=w, q_scale=qs, k_scale=ks)
+    out = dict(q=q, k=k, w=w, q_scale=qs, k_scale=ks)
+    if inp.dtype in ("mxfp8", "mxfp4"):
+        out["fmt"] = inp.dtype
+    return out
 
 
 def oracle_rows(inp: datagen.Inputs, queries) -> list:

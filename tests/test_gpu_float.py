@@ -50,6 +50,8 @@ def _run_config(hk, name, nsub, with_baseline):
     rows = oracle_rows(inp, sub)
     say(f"{name}: hytopk_select + replay")
     kw = dict(q_scale=dv["q_scale"], k_scale=dv["k_scale"])
+    if "fmt" in dv:
+        kw["fmt"] = dv["fmt"]
     idx, sc, st = hk.select(dv["q"], dv["k"], dv["w"], inp.k, with_stats=True, **kw)
     rep = hk.replay(dv["q"], dv["k"], dv["w"], idx, **kw)
     torch.cuda.synchronize()
@@ -86,3 +88,11 @@ def test_glm1m_bf16(hk):
 
 def test_glm1m_fp8(hk):
     _run_config(hk, "glm1m_fp8", 64, with_baseline=False)
+
+
+def test_glm1m_mxfp8(hk):
+    _run_config(hk, "glm1m_mxfp8", 32, with_baseline=False)
+
+
+def test_glm1m_mxfp4(hk):
+    _run_config(hk, "glm1m_mxfp4", 32, with_baseline=True)
