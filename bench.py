@@ -26,7 +26,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 if ROOT not in sys.path:
     sys.path.insert(0, ROOT)
 
-PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2}   # MI355X dense MFMA
+PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "mxfp8": 5033.2, "mxfp4": 10066.3}  # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "HyTopK select ms + TFLOP/s (%MFMA peak) at L=1M,n=8192,k=2048; replay ms"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_score_tile_glm1m_bf16.txt")
@@ -51,10 +51,13 @@ def sum_ctx(q_start: int, n: int) -> int:
     return n * (q_start + 1) + n * (n - 1) // 2
 
 
-def replay_bytes(n, H, d, k, fp8) -> int:
-    bk = 1 if fp8 else 2
-    per_entry = d * bk + 4 + 4 + (4 if fp8 else 0)
-    per_query = H * (d * bk + 4) + (4 if fp8 else 0)
+def replay_bytes(n, H, d, k, fmt) -> int:
+    """Algorithmic bytes of replay: per entry the key row (+ its scales), the
+    index and the output score; per query its rows (+ scales) and weights."""
+    row = {"bf16": 2 * d, "fp8": d, "mxfp8": d + d // 32, "mxfp4": d // 2 + d // 32}[fmt]
+    tok = 4 if fmt == "fp8" else 0   # per-token fp32 scale
+    per_entry = row + tok + 4 + 4
+    per_query = H * (row + 4) + tok
     return n * k * per_entry + n * per_query
 
 
@@ -136,11 +139,17 @@ def main() -> int:
     torch.cuda.set_device(0)
     log(f"generating {args.workload}")
     inp = datagen.make(args.workload)
-    fp8 = inp.dtype == "fp8"
+    fmt = inp.dtype
+    fp8 = fmt != "bf16"
     dev = "cuda:0"
-    if fp8:
+    if fmt == "fp8":
         q = torch.from_numpy(inp.q).to(dev).view(torch.float8_e4m3fn)
         k = torch.from_numpy(inp.k_).to(dev).view(torch.float8_e4m3fn)
+        qs = torch.from_numpy(inp.q_scale).to(dev)
+        ks = torch.from_numpy(inp.k_scale).to(dev)
+    elif fmt in ("mxfp8", "mxfp4"):
+        q = torch.from_numpy(inp.q).to(dev)
+        k = torch.from_numpy(inp.k_).to(dev)
         qs = torch.from_numpy(inp.q_scale).to(dev)
         ks = torch.from_numpy(inp.k_scale).to(dev)
     else:
@@ -148,16 +157,17 @@ def main() -> int:
         k = torch.from_numpy(inp.k_.view(np.int16)).to(dev).view(torch.bfloat16)
         qs = ks = None
     w = torch.from_numpy(inp.w).to(dev)
+    fk = dict(fmt=fmt) if fmt in ("mxfp8", "mxfp4") else {}
     hk.load_library()
-    ws = torch.empty(hk.select_workspace_bytes(q, k, w, inp.k), dtype=torch.uint8, device=dev)
+    ws = torch.empty(hk.select_workspace_bytes(q, k, w, inp.k, **fk), dtype=torch.uint8, device=dev)
     idx = torch.empty((inp.n, inp.k), dtype=torch.int32, device=dev)
     sc = torch.empty((inp.n, inp.k), dtype=torch.float32, device=dev)
     rep = torch.empty_like(sc)
 
     def step():
         _, _, st = hk.select(q, k, w, inp.k, q_scale=qs, k_scale=ks, workspace=ws, out=(idx, sc),
-                             with_stats=True)
-        hk.replay(q, k, w, idx, q_scale=qs, k_scale=ks, out=rep)
+                             with_stats=True, **fk)
+        hk.replay(q, k, w, idx, q_scale=qs, k_scale=ks, out=rep, **fk)
         return st
 
     log(f"warmup {args.warmup}")
@@ -177,9 +187,9 @@ def main() -> int:
     for i in range(args.steps):
         ev[i][0].record()
         _, _, stats = hk.select(q, k, w, inp.k, q_scale=qs, k_scale=ks, workspace=ws,
-                                out=(idx, sc), with_stats=True)
+                                out=(idx, sc), with_stats=True, **fk)
         ev[i][1].record()
-        hk.replay(q, k, w, idx, q_scale=qs, k_scale=ks, out=rep)
+        hk.replay(q, k, w, idx, q_scale=qs, k_scale=ks, out=rep, **fk)
         ev[i][2].record()
     t_end.record()
     torch.cuda.synchronize()
@@ -193,10 +203,10 @@ def main() -> int:
     q_start = inp.L - inp.n
     sel_flops = scoring_flops(inp.L, inp.n, inp.H, inp.d, q_start)
     rep_flops = 2.0 * inp.H * inp.d * inp.n * inp.k
-    peak = PEAK_TFLOPS["fp8" if fp8 else "bf16"]
+    peak = PEAK_TFLOPS[fmt]
     value = (sel_flops + rep_flops) / (ms_per_step * 1e-3) / 1e12
     sel_tflops = sel_flops / (select_ms * 1e-3) / 1e12
-    rbytes = replay_bytes(inp.n, inp.H, inp.d, inp.k, fp8)
+    rbytes = replay_bytes(inp.n, inp.H, inp.d, inp.k, fmt)
     replay_gbs = rbytes / (replay_ms * 1e-3) / 1e9
 
     launches, score_total = phases.get("score_compact", (0, 0.0))
@@ -215,14 +225,16 @@ def main() -> int:
     baseline_ms = None
     if not args.no_baseline:
         log("baseline: materialise the score table, then row top-k")
-        bws = torch.empty(hk.baseline_workspace_bytes(q, k, w, inp.k), dtype=torch.uint8, device=dev)
+        bws = torch.empty(hk.baseline_workspace_bytes(q, k, w, inp.k, **fk), dtype=torch.uint8, device=dev)
         bidx = torch.empty_like(idx)
         bsc = torch.empty_like(sc)
-        hk.baseline_select(q, k, w, inp.k, q_scale=qs, k_scale=ks, workspace=bws, out=(bidx, bsc))
+        hk.baseline_select(q, k, w, inp.k, q_scale=qs, k_scale=ks, workspace=bws, out=(bidx, bsc),
+                           **fk)
         torch.cuda.synchronize()
         a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
         a.record()
-        hk.baseline_select(q, k, w, inp.k, q_scale=qs, k_scale=ks, workspace=bws, out=(bidx, bsc))
+        hk.baseline_select(q, k, w, inp.k, q_scale=qs, k_scale=ks, workspace=bws, out=(bidx, bsc),
+                           **fk)
         b.record()
         torch.cuda.synchronize()
         baseline_ms = a.elapsed_time(b)
@@ -278,7 +290,7 @@ def main() -> int:
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "fp8_e4m3" if fp8 else "bf16",
+        "dtype": {"bf16": "bf16", "fp8": "fp8_e4m3", "mxfp8": "mxfp8_e4m3", "mxfp4": "mxfp4_e2m1"}[fmt],
         "data": "synthetic (seeded datagen; no dataset or weights)",
         "config": {"workload": f"{args.workload}: L={inp.L} n={inp.n} (positions {q_start}..{inp.L - 1}) "
                                f"H={inp.H} d={inp.d} k={inp.k}",

@@ -196,9 +196,10 @@ def select_workspace_bytes(q, k, w, topk: int, q_start=None, params=None, q_pos=
     return int(lib.hytopk_select_workspace(ctypes.byref(prob), ctypes.byref(prm) if prm else None))
 
 
-def baseline_workspace_bytes(q, k, w, topk: int, q_start=None) -> int:
+def baseline_workspace_bytes(q, k, w, topk: int, q_start=None, fmt=None) -> int:
     lib = load_library()
-    return int(lib.hytopk_baseline_workspace(ctypes.byref(_problem(q, k, w, topk, q_start))))
+    return int(lib.hytopk_baseline_workspace(ctypes.byref(_problem(q, k, w, topk, q_start,
+                                                                   fmt=fmt))))
 
 
 def select(q, k, w, topk: int, *, q_scale=None, k_scale=None, q_start=None, params=None,

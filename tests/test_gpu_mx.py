@@ -76,7 +76,8 @@ def test_mx_gaussian_blocks_follow_their_scales(hk, fmt):
     from gpu_util import assert_float_row
     say(f"mx: {fmt} Gaussian problem L=20000 n=64 H=64 d=128 k=512")
     inp = datagen.make_custom("mxg", 20000, 64, 64, 128, 512, dtype=fmt, dist="normal", seed=94)
-    assert np.unique(inp.k_scale).size > 3 and np.unique(inp.q_scale).size > 3
+    # block maxima of Gaussian values span a few binades: several distinct scales
+    assert np.unique(inp.k_scale).size >= 3 and np.unique(inp.q_scale).size >= 3
     dv = to_device(inp)
     kw = dict(q_scale=dv["q_scale"], k_scale=dv["k_scale"], fmt=fmt)
     idx, sc = hk.select(dv["q"], dv["k"], dv["w"], inp.k, **kw)
