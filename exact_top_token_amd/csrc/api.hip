@@ -189,8 +189,9 @@ int check_inputs(const hytopk_problem* p, const void* q, const void* qs, const v
 }
 
 // Splits of the key range so that the score launch has enough workgroups.
-void splits(int64_t nq, int64_t maxctx, int& nsplit, int& split_len) {
-  const int64_t groups = (nq + 15) / 16;
+void splits(int64_t nq, int64_t maxctx, int fmt, int& nsplit, int& split_len) {
+  const int64_t gq = hk::score_group_queries(fmt);
+  const int64_t groups = (nq + gq - 1) / gq;
   int64_t want = (512 + groups - 1) / groups;
   const int64_t most = std::max<int64_t>(1, (maxctx + 4095) / 4096);
   want = std::max<int64_t>(1, std::min(want, most));
@@ -256,7 +257,7 @@ int rows_path(const hytopk_problem* p, const hk::ScoreArgs& base, const int* qli
   a.qlist = qlist;
   a.q_offset = q_offset;
   a.nq = nq;
-  splits(nq, maxctx, a.nsplit, a.split_len);
+  splits(nq, maxctx, p->dtype, a.nsplit, a.split_len);
   {
     Span sp("score_rows", s);
     HK_HIP(hk::launch_score(a, p->d, p->dtype, s), "score rows launch");
@@ -384,7 +385,7 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
     a.cand = cand;
     a.cap = r.cap;
     a.nq = n;
-    splits(n, maxctx, a.nsplit, a.split_len);
+    splits(n, maxctx, p->dtype, a.nsplit, a.split_len);
     {
       Span sp("score_compact", s);
       HK_HIP(hk::launch_score(a, p->d, fmt, s), "fused score launch");

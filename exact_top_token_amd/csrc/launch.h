@@ -40,6 +40,7 @@ struct ScoreArgs {
 };
 
 hipError_t launch_score(const ScoreArgs& a, int d, int fmt, hipStream_t s);
+int score_group_queries(int fmt);  // queries per workgroup of the score kernel
 
 // Per-query sampled threshold: tau[q] = the r-th largest of the M_q sample
 // scores at positions floor(j * ctx / M_q).

@@ -1,8 +1,9 @@
 // Fused indexer scoring over causal key ranges (the hot loop of HyTopK).
 //
-// A workgroup of 8 waves owns 16 queries (8 query pairs, one pair per wave,
-// queries held in registers as MFMA A operands) and streams key tiles of 64
-// keys through LDS; every key tile is read from memory once per 16 queries.
+// A workgroup of 8 waves (4 for the scaled formats) owns 16 (8) queries, one
+// query pair per wave held in registers as MFMA A operands, and streams key
+// tiles of 64 keys through LDS; every key tile is read from memory once per
+// workgroup.
 // Per 16-key column block each wave runs 8 x 4 MFMAs (bf16, H = 64, d = 128),
 // applies ReLU and the weighted head sum in registers and then either
 //   COMPACT: compares each score with the query's sampled threshold and
@@ -21,7 +22,17 @@
 namespace hk {
 
 constexpr int kTK = 64;          // keys per LDS stage
-constexpr int kThreads = 512;    // 8 waves = 8 query pairs
+// Waves per workgroup, one query pair each: 8 for bf16; 4 for the scaled
+// formats, whose epilogue outweighs their MFMAs -- two independent groups per
+// CU then drift out of phase and one group's epilogue overlaps the other's
+// MFMAs (measured at the 1M shape: FP8 -3%, MXFP8 -8%, MXFP4 -4% time; bf16
+// +4.5%, so it keeps one group of 8).
+template <int FMT>
+struct Group {
+  static constexpr int WAVES = FMT == kBF16 ? 8 : 4;
+  static constexpr int THREADS = 64 * WAVES;
+  static constexpr int QUERIES = 2 * WAVES;
+};
 constexpr int kSB = 128;         // staged candidates per query before a flush
 
 #define HK_LDS(x) ((__attribute__((address_space(3))) void*)(x))
@@ -34,7 +45,10 @@ constexpr int kSB = 128;         // staged candidates per query before a flush
 // one workgroup barrier per tile.  The stages are distinct LDS objects so the
 // compiler can tell the loads into one stage from reads of another.
 template <int RB, int D, int FMT, bool ROWS>
-__global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
+__global__ void __launch_bounds__(Group<FMT>::THREADS) __attribute__((amdgpu_waves_per_eu(2)))
+score_tile_kernel(ScoreArgs a) {
+  constexpr int kWaves = Group<FMT>::WAVES, kThreads = Group<FMT>::THREADS;
+  constexpr int kGroupQ = Group<FMT>::QUERIES;
   using T = PairTile<RB, D, FMT>;
   using F = Fmt<FMT>;
   using Frag = typename T::Frag;
@@ -52,13 +66,13 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t t1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t t2[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t t3[TILE_BYTES];
-  __shared__ uint2 stage[ROWS ? 1 : 8][2][kSB];
-  __shared__ int s_maxt[8];
-  __shared__ int s_minlo[8];
+  __shared__ uint2 stage[ROWS ? 1 : kWaves][2][kSB];
+  __shared__ int s_maxt[kWaves];
+  __shared__ int s_minlo[kWaves];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4;
   const int group = blockIdx.x / a.nsplit, split = blockIdx.x % a.nsplit;
-  const int e0 = group * 16 + wave * 2;
+  const int e0 = group * kGroupQ + wave * 2;
   const int ea = e0 < a.nq ? e0 : -1;
   const int eb = e0 + 1 < a.nq ? e0 + 1 : -1;
   const int qa = ea < 0 ? -1 : (a.qlist ? a.qlist[ea] : a.q_offset + ea);
@@ -77,7 +91,7 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
   __syncthreads();
   int maxt = s_maxt[0], minlo = s_minlo[0];
 #pragma unroll
-  for (int w = 1; w < 8; ++w) {
+  for (int w = 1; w < kWaves; ++w) {
     maxt = max(maxt, s_maxt[w]);
     minlo = min(minlo, s_minlo[w]);
   }
@@ -88,7 +102,7 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
   if (kb >= ke) return;  // uniform over the workgroup
   const int ntiles = (ke - kb + TK - 1) / TK;
 
-  // DMA layout: load p of wave w fills 1 KB block p * 8 + w of a stage; its
+  // DMA layout: load p of wave w fills 1 KB block p * kWaves + w of a stage; its
   // lane j lands on key kk = block * KPB + j / NCH, 16-byte slot j % NCH,
   // and fetches chunk (slot ^ (kk % NCH)) of that key: the swizzle the B
   // fragment reads undo.  kk % NCH does not depend on p.
@@ -100,10 +114,10 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
     const uint8_t* base = a.k + (int64_t)k0 * RBYTES;
 #pragma unroll
     for (int p = 0; p < OPS; ++p) {
-      const int kk = dma_kk + p * 8 * KPB;
+      const int kk = dma_kk + p * kWaves * KPB;
       int off = kk * RBYTES + dma_c;
       if (tile >= full_tiles) off = (min(k0 + kk, a.L - 1) - k0) * RBYTES + dma_c;  // never past L
-      __builtin_amdgcn_global_load_lds(base + off, HK_LDS(buf + (p * 8 + wave) * 1024), 16, 0, 0);
+      __builtin_amdgcn_global_load_lds(base + off, HK_LDS(buf + (p * kWaves + wave) * 1024), 16, 0, 0);
     }
   };
   issue(0, t0);
@@ -260,8 +274,9 @@ __global__ void __launch_bounds__(kThreads) score_tile_kernel(ScoreArgs a) {
 
 template <int RB, int D, int FMT>
 static hipError_t launch_rb(const ScoreArgs& a, hipStream_t s) {
-  const int groups = (a.nq + 15) / 16;
-  dim3 grid((unsigned)(groups * a.nsplit)), block(kThreads);
+  constexpr int gq = Group<FMT>::QUERIES;
+  const int groups = (a.nq + gq - 1) / gq;
+  dim3 grid((unsigned)(groups * a.nsplit)), block(Group<FMT>::THREADS);
   if (a.rows) {
     hipLaunchKernelGGL((score_tile_kernel<RB, D, FMT, true>), grid, block, 0, s, a);
   } else {
@@ -288,6 +303,10 @@ hipError_t launch_score(const ScoreArgs& a, int d, int fmt, hipStream_t s) {
   if (fmt == kMXFP8) return launch_d128<kMXFP8>(a, small, s);
   if (fmt == kMXFP4) return launch_d128<kMXFP4>(a, small, s);
   return hipErrorInvalidValue;
+}
+
+int score_group_queries(int fmt) {
+  return fmt == kBF16 ? Group<kBF16>::QUERIES : Group<kFP8>::QUERIES;
 }
 
 }  // namespace hk
