@@ -92,7 +92,7 @@ constexpr size_t kAlign = 256;
 constexpr int kMaxK = 2048;
 constexpr int kMaxCap = 16384;
 constexpr int kMaxM = 16384;
-constexpr size_t kLdsLimit = 160 * 1024 - 8 * 1024;  // gfx950 LDS minus static scratch
+constexpr size_t kLdsLimit = 160 * 1024 - 10 * 1024;  // gfx950 LDS minus static scratch
 
 size_t align_up(size_t x) { return (x + kAlign - 1) / kAlign * kAlign; }
 

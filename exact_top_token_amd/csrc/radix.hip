@@ -29,79 +29,102 @@ constexpr int kMaxRounds = 4;  // k <= 2048 = kMaxRounds * kSelThreads
 // ----------------------------------------------------------------- helpers
 
 struct SortScratch {
-  int cnt[16][kMaxRounds][kSelWaves];  // per (digit, round, wave) counts, then offsets
+  int cnt[256 * kSelWaves];  // per (digit, wave) counts, then offsets
   int wsum[kSelWaves];
   int skip;
 };
 
-// Exclusive scan, in place, of `m` ints of `v` (m <= 2 * kSelThreads).
+// Exclusive scan, in place, of `m` ints of `v` (m <= 4 * kSelThreads).
 __device__ void block_scan_excl(int* v, int m, int* wsum) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int i0 = 2 * tid, i1 = 2 * tid + 1;
-  const int a0 = i0 < m ? v[i0] : 0;
-  const int a1 = i1 < m ? v[i1] : 0;
-  const int loc = a0 + a1;
+  int a[4];
+  int loc = 0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 4 * tid + j;
+    a[j] = i < m ? v[i] : 0;
+    loc += a[j];
+  }
   const int pre = wave_prefix_excl(loc);
   if (lane == kWave - 1) wsum[wave] = pre + loc;
   __syncthreads();
-  int base = 0;
+  int base = pre;
   for (int w = 0; w < wave; ++w) base += wsum[w];
-  if (i0 < m) v[i0] = base + pre;
-  if (i1 < m) v[i1] = base + pre + a0;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int i = 4 * tid + j;
+    if (i < m) v[i] = base;
+    base += a[j];
+  }
   __syncthreads();
 }
 
-// Stable LSD radix sort, ascending by key bits [lo, hi) in 4-bit digits, of
-// the N (key, val) pairs in (k0, v0); (k1, v1) is scratch of the same size.
-// Returns true when the result ended in (k1, v1).
+// Stable LSD radix sort, ascending by key bits [lo, hi), of the N <= 2048
+// (key, val) pairs in (k0, v0); (k1, v1) is scratch of the same size.
+// Digits are up to 8 bits wide (the passes split [lo, hi) evenly).  Wave w
+// ranks entries 256 w .. 256 w + 255 in four rounds of 64: the lanes holding
+// the same digit are found with one ballot per digit bit, and a per-(digit,
+// wave) running count in LDS carries the rank across rounds, so entries with
+// equal digits keep their order.  Returns true when the result ended in
+// (k1, v1).
 __device__ __forceinline__ bool block_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int N,
                                  int lo, int hi, SortScratch& ss) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int rounds = (N + kSelThreads - 1) / kSelThreads;
   const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
   bool flipped = false;
-  for (int sh = lo; sh < hi; sh += 4) {
-    int myd[kMaxRounds], myrank[kMaxRounds];
+  const int passes = (hi - lo + 7) / 8;
+  int sh = lo;
+  for (int p = 0; p < passes; ++p) {
+    const int w = (hi - sh + (passes - p) - 1) / (passes - p);  // digit bits of this pass
+    const int nd = 1 << w;
+    const uint32_t dmask = (uint32_t)nd - 1u;
+    for (int b = tid; b < nd * kSelWaves; b += kSelThreads) ss.cnt[b] = 0;
+    if (tid == 0) ss.skip = 0;
+    __syncthreads();
+    uint32_t myd[kMaxRounds];
+    int myrank[kMaxRounds];
 #pragma unroll
     for (int j = 0; j < kMaxRounds; ++j) {
-      const int i = j * kSelThreads + tid;
-      const bool ok = j < rounds && i < N;
-      const int d = ok ? (int)((k0[i] >> sh) & 15u) : 16;
+      const int i = wave * (kMaxRounds * kWave) + j * kWave + lane;
+      const bool ok = i < N;
+      const uint32_t d = ok ? (k0[i] >> sh) & dmask : 0u;
+      uint64_t m = __ballot(ok);
+      for (int b = 0; b < w; ++b) {
+        const bool bit = (d >> b) & 1u;
+        const uint64_t bb = __ballot(bit);
+        m &= bit ? bb : ~bb;
+      }
       int rank = 0;
-#pragma unroll
-      for (int b = 0; b < 16; ++b) {
-        const uint64_t mb = __ballot(d == b);
-        if (d == b) rank = __popcll(mb & lt);
-        if (lane == 0 && j < rounds) ss.cnt[b][j][wave] = __popcll(mb);
+      if (ok) {
+        const int before = ss.cnt[d * kSelWaves + wave];
+        rank = before + __popcll(m & lt);
+        // the lowest lane of each digit group advances the running count
+        if ((m & lt) == 0ull) ss.cnt[d * kSelWaves + wave] = before + __popcll(m);
       }
       myd[j] = d;
       myrank[j] = rank;
     }
-    if (tid == 0) ss.skip = 0;
     __syncthreads();
     // A pass whose digit is the same for all N entries leaves the order alone.
-    if (tid < 16) {
+    for (int dd = tid; dd < nd; dd += kSelThreads) {
       int tot = 0;
-      for (int j = 0; j < rounds; ++j)
-        for (int w = 0; w < kSelWaves; ++w) tot += ss.cnt[tid][j][w];
+#pragma unroll
+      for (int v = 0; v < kSelWaves; ++v) tot += ss.cnt[dd * kSelWaves + v];
       if (tot == N) ss.skip = 1;
     }
     __syncthreads();
     const bool skip = ss.skip != 0;
-    __syncthreads();  // everyone has read the flag before thread 0 resets it
-    if (skip) continue;  // uniform
-    // Offsets in (digit, round, wave) order; unused rounds hold zero counts.
-    for (int b = tid; b < 16 * kMaxRounds * kSelWaves; b += kSelThreads) {
-      const int j = (b / kSelWaves) % kMaxRounds;
-      if (j >= rounds) (&ss.cnt[0][0][0])[b] = 0;
+    sh += w;
+    if (skip) {  // uniform
+      __syncthreads();  // everyone has read the flag before thread 0 resets it
+      continue;
     }
-    __syncthreads();
-    block_scan_excl(&ss.cnt[0][0][0], 16 * kMaxRounds * kSelWaves, ss.wsum);
+    block_scan_excl(ss.cnt, nd * kSelWaves, ss.wsum);
 #pragma unroll
     for (int j = 0; j < kMaxRounds; ++j) {
-      const int i = j * kSelThreads + tid;
-      if (j < rounds && i < N) {
-        const int dst = ss.cnt[myd[j]][j][wave] + myrank[j];
+      const int i = wave * (kMaxRounds * kWave) + j * kWave + lane;
+      if (i < N) {
+        const int dst = ss.cnt[myd[j] * kSelWaves + wave] + myrank[j];
         k1[dst] = k0[i];
         v1[dst] = v0[i];
       }
