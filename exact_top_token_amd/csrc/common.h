@@ -163,11 +163,24 @@ __device__ uint32_t block_select_largest(int m, int r, KeyF key, TakeF take, Rad
     const int shift = 8 * pass;
     for (int b = tid; b < 256; b += nt) sc.hist[b] = 0;
     __syncthreads();
+    // Each thread counts runs of equal digits among its entries and adds a
+    // run with one atomic: in the passes where most entries share a digit
+    // this avoids serialising every lane on one LDS address.
+    uint32_t run_d = 0u;
+    int run_n = 0;
     for (int i = tid; i < m; i += nt) {
       if (!take(i)) continue;
       const uint32_t kk = key(i);
-      if ((kk & pmask) == prefix) atomicAdd(&sc.hist[(kk >> shift) & 255u], 1);
+      if ((kk & pmask) != prefix) continue;
+      const uint32_t d = (kk >> shift) & 255u;
+      if (run_n > 0 && d != run_d) {
+        atomicAdd(&sc.hist[run_d], run_n);
+        run_n = 0;
+      }
+      run_d = d;
+      ++run_n;
     }
+    if (run_n > 0) atomicAdd(&sc.hist[run_d], run_n);
     __syncthreads();
     int h = 0, suf = 0;
     if (tid < 256) {

@@ -196,7 +196,14 @@ __global__ void __launch_bounds__(kSampleThreads) sample_tau_kernel(SampleArgs a
   __shared__ RadixScratch sc;
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int q = blockIdx.x;
+  // Workgroups are dispatched to the 8 XCDs round-robin; each XCD takes a
+  // contiguous run of queries instead, whose sample positions nearly
+  // coincide, so that their key gathers hit that XCD's own L2.
+  const int q = [] {
+    const int nx = 8, b = blockIdx.x, x = b % nx;
+    const int base = (int)gridDim.x / nx, extra = (int)gridDim.x % nx;
+    return x * base + min(x, extra) + b / nx;
+  }();
   const QRange rg = query_range(a.qpos, a.qfirst, a.q_start, a.L, q);
   const int ctx = rg.hi - rg.lo + 1;
   if (ctx <= 0) {  // empty context: nothing passes, nothing is needed (uniform)

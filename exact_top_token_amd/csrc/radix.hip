@@ -264,11 +264,24 @@ __global__ void __launch_bounds__(kSelThreads) cand_select_kernel(const int* cnt
   uint32_t* sp = sk + topk;         // [topk] kept positions
   const uint2* src = cand + (int64_t)q * cap;
   uint32_t lo = 0xFFFFFFFFu, hi = 0u;
-  for (int i = tid; i < c; i += kSelThreads) {
-    const uint32_t kk = score_key(__uint_as_float(src[i].y));
-    ck[i] = kk;
-    lo = min(lo, kk);
-    hi = max(hi, kk);
+  constexpr int kU = 4;  // candidate loads in flight per thread
+  for (int i0 = tid; i0 < c; i0 += kU * kSelThreads) {
+    uint32_t y[kU];
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = i0 + u * kSelThreads;
+      y[u] = i < c ? src[i].y : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = i0 + u * kSelThreads;
+      if (i < c) {
+        const uint32_t kk = score_key(__uint_as_float(y[u]));
+        ck[i] = kk;
+        lo = min(lo, kk);
+        hi = max(hi, kk);
+      }
+    }
   }
   if (tid == 0) sh.nsel = 0;
   uint32_t kmin, kmax;
@@ -290,23 +303,32 @@ __global__ void __launch_bounds__(kSelThreads) cand_select_kernel(const int* cnt
         rr, mm, (int)pb);
   }
   // compaction: one slot reservation per wave and sweep
-  for (int i0 = 0; i0 < c; i0 += kSelThreads) {
-    const int i = i0 + tid;
-    bool keep = false;
-    uint32_t kk = 0u;
-    if (i < c) {
-      kk = ck[i];
-      keep = kk > v || (kk == v && (pmax == 0xFFFFFFFFu || src[i].x <= pmax));
+  for (int j0 = 0; j0 < c; j0 += kU * kSelThreads) {
+    uint32_t px[kU];  // positions, loaded ahead of the sweeps that use them
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = j0 + u * kSelThreads + tid;
+      px[u] = i < c ? src[i].x : 0u;
     }
-    const uint64_t m = __ballot(keep);
-    int base = 0;
-    if (lane == 0 && m) base = atomicAdd(&sh.nsel, __popcll(m));
-    base = __shfl(base, 0);
-    if (keep) {
-      const int slot = base + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
-      if (slot < need) {  // exactly `need` entries qualify; the guard keeps LDS writes in bounds
-        sk[slot] = kk;
-        sp[slot] = src[i].x;
+#pragma unroll
+    for (int u = 0; u < kU; ++u) {
+      const int i = j0 + u * kSelThreads + tid;
+      bool keep = false;
+      uint32_t kk = 0u;
+      if (i < c) {
+        kk = ck[i];
+        keep = kk > v || (kk == v && (pmax == 0xFFFFFFFFu || px[u] <= pmax));
+      }
+      const uint64_t m = __ballot(keep);
+      int base = 0;
+      if (lane == 0 && m) base = atomicAdd(&sh.nsel, __popcll(m));
+      base = __shfl(base, 0);
+      if (keep) {
+        const int slot = base + __popcll(m & ((lane == 0) ? 0ull : (~0ull >> (64 - lane))));
+        if (slot < need) {  // exactly `need` entries qualify; the guard keeps LDS writes in bounds
+          sk[slot] = kk;
+          sp[slot] = px[u];
+        }
       }
     }
   }
