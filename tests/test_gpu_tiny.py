@@ -107,6 +107,7 @@ def test_tiny_reproducible(hk, tiny):
     (777, 77, 4, 64, 700, 7),       # k close to ctx, small heads
     (5000, 130, 8, 128, 1, 8),      # k = 1
     (4100, 33, 64, 64, 2048, 9),    # k = 2048 at H = 64, d = 64
+    (64, 5, 4, 64, 16, 10),         # fewer queries than XCDs (sampling workgroup map)
 ])
 def test_ragged_shapes_bit_exact(hk, L, n, H, d, k, seed):
     say(f"ragged: L={L} n={n} H={H} d={d} k={k} seed={seed}")
