@@ -113,8 +113,9 @@ def main() -> int:
                          "the HBM byte counters of a profiler run) and exit")
     args = ap.parse_args()
     if args.gpus != 1:
-        print("bench.py measures one GPU: the selection path has no multi-GPU mode in this "
-              "build (see the sharding notes in DESIGN.md); run with --gpus 1", file=sys.stderr)
+        print("bench.py measures one GPU: the selection path has no multi-GPU mode (each "
+              "GPU would select for its own query shard after an all-gather of the keys); "
+              "run with --gpus 1", file=sys.stderr)
         return 2
 
     import numpy as np
