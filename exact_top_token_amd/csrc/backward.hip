@@ -1,6 +1,6 @@
 // Indexer backward at the replayed entries ("HyScale sparse-attention
 // training -- Selection without a score table", key-observation paragraph:
-// the indexer's loss reads only the scores at the selected entries and the
+// the indexer's loss depends on the scores of the selected entries alone, and the
 // top-k choice carries no gradient).  Given dI[t, j], the upstream gradient
 // of the replayed score I(t, idx[t, j]), with c[h, j] = q[t, h] . k[idx[t, j]]
 // and ReLU'(c) = [c > 0]:

@@ -9,10 +9,10 @@
 //   makes the output bitwise reproducible:
 //     1. radix select of the k-th largest order-preserving score key;
 //     2. at that score, radix select over positions keeps the lowest-position
-//        ties ("resolves ties at the k-th score with a radix select over
-//        positions");
+//        ties (the pages break ties at the k-th score by position, with a
+//        radix select);
 //     3. LSD radix sort of the kept k by (score descending, position
-//        ascending) ("orders the k kept entries with a radix sort").
+//        ascending) (the pages order the kept entries with a radix sort).
 // * row_topk: the same result from materialised score rows (the conventional
 //   two-kernel route, recovery and full rescore): radix select over the row,
 //   emission of the kept entries in position order (ties: first ones win),

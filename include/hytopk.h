@@ -16,8 +16,9 @@
  *     than 64 queries fail, ties at the k-th score resolved by a radix select
  *     over positions, and a radix sort of the kept k (same page, HyTopK
  *     paragraph; the paper's abstract).
- *   * Selection replay keeps the k indices per query and, in recomputation,
- *     rescores only those entries (same page, selection-replay paragraph).
+ *   * Replay: the k selected indices of each query are saved, and the
+ *     recomputation pass scores just those entries again (same page,
+ *     selection-replay paragraph).
  *
  * Indexer: I(t,s) = sum_h w[t,h] * ReLU(q[t,h] . k[s]), for key positions
  * s = 0..t (a query sees itself and every earlier key).  Result order: score
@@ -185,8 +186,8 @@ int hytopk_baseline_select(const hytopk_problem* p, const void* q, const void* q
 size_t hytopk_backward_workspace(const hytopk_problem* p);
 
 /* Indexer backward at the replayed entries (HyScale explainer, key-observation
- * paragraph: the indexer's loss reads only the scores at the selected entries,
- * and the top-k choice itself carries no gradient).  With d_score [n][k] fp32
+ * paragraph: the indexer's loss depends only on the scores of the selected
+ * entries, and the top-k choice itself carries no gradient).  With d_score [n][k] fp32
  * the upstream gradient of the replayed scores I(q_start + i, idx[i][j]),
  * c = q[i][h] . k[idx[i][j]] and ReLU'(c) = [c > 0] (0 at c == 0):
  *   dw [n][H]    fp32: dw[i][h]    = sum_j d_score[i][j] * max(c, 0)

@@ -29,8 +29,8 @@ score table]:
 2. score every causal pair (query position t sees keys 0..t; with packed
    sequences, the keys from its own sequence's first key through t) with the
    learned-sparse-attention indexer I(t,s) = sum_h w[t,h] * ReLU(q[t,h] . k[s]).
-   The pages do not print the indexer's formula; they say its scores are the
-   same kind of work as attention scores [Explainer, contest] and that the
+   The pages do not print the indexer's formula; they liken the cost of its
+   scores to that of attention scores [Explainer, contest] and say that the
    architecture descends from DeepSeek-V3.2 [Abstract].  This is the standard
    form of that indexer: the head weight applies after the ReLU;
 3. order the context by score descending, then position ascending (lower
@@ -39,8 +39,8 @@ score table]:
 5. backward at the replayed entries: given an upstream gradient dI[t, j] for
    the score at idx[t, j], the gradients of sum_{t,j} dI[t,j] * I(t, idx[t,j])
    with respect to q, w and k.  The choice itself carries no gradient (top-k
-   is not differentiable) and the indexer's loss reads only the scores at the
-   selected entries, so nothing else enters [Explainer, key observation].
+   is not differentiable) and the indexer's loss depends on the selected
+   entries' scores alone, so nothing else enters [Explainer, key observation].
 
 The threshold model (``sample_count`` .. ``predict_paths``) is not part of the
 result.  It restates the HyTopK paragraph and the worked example so tests can
