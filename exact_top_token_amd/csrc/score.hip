@@ -6,12 +6,10 @@
 // workgroup.
 // Per 16-key column block each wave runs 8 x 4 MFMAs (bf16, H = 64, d = 128),
 // applies ReLU and the weighted head sum in registers and then either
-//   COMPACT: compares each score with the query's sampled threshold and
-//     appends the passing keys to a per-wave LDS staging area; full stages are
-//     flushed with one atomicAdd on the query's global candidate counter and
-//     a copy into the candidate buffer ("compares each score with the
-//     threshold on chip and writes only the keys that pass into a small
-//     candidate buffer": HyScale explainer, HyTopK paragraph);
+//   COMPACT: compares each score with the query's sampled threshold in
+//     registers and emits only the passing keys into the query's bounded
+//     candidate buffer, so no score table is written (HyScale explainer,
+//     HyTopK paragraph);
 //   ROWS: writes the score to a full score row (the conventional table of the
 //     explainer's contest paragraph; also the recovery and full-rescore path).
 // Both modes share the scoring code, so a query's scores are bit-identical on
@@ -44,7 +42,12 @@ constexpr int kSB = 128;         // staged candidates per query before a flush
 // (global_load_lds_dwordx4), three tiles ahead of the one being scored, with
 // one workgroup barrier per tile.  The stages are distinct LDS objects so the
 // compiler can tell the loads into one stage from reads of another.
-template <int RB, int D, int FMT, bool ROWS>
+// OWN (COMPACT with one key split): each wave is the only writer of its two
+// queries' candidates, so it keeps their counts in registers and every
+// passing lane stores its candidate straight to its slot; with several
+// splits per query, candidates are staged per wave in LDS and flushed with
+// one atomicAdd on the query's count.
+template <int RB, int D, int FMT, bool ROWS, bool OWN>
 __global__ void __launch_bounds__(Group<FMT>::THREADS) __attribute__((amdgpu_waves_per_eu(2)))
 score_tile_kernel(ScoreArgs a) {
   constexpr int kWaves = Group<FMT>::WAVES, kThreads = Group<FMT>::THREADS;
@@ -66,7 +69,7 @@ score_tile_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t t1[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t t2[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t t3[TILE_BYTES];
-  __shared__ uint2 stage[ROWS ? 1 : kWaves][2][kSB];
+  __shared__ uint2 stage[(ROWS || OWN) ? 1 : kWaves][2][(ROWS || OWN) ? 1 : kSB];
   __shared__ int s_maxt[kWaves];
   __shared__ int s_minlo[kWaves];
 
@@ -138,7 +141,7 @@ score_tile_kernel(ScoreArgs a) {
   if (!ROWS) tau = qs >= 0 ? a.tau[qs] : 0.0f;
   const bool owner = (lane & 16) == 0;  // lanes 0..15 and 32..47 own distinct (query, key)
 
-  int cntA = 0, cntB = 0;  // staged candidates (wave-uniform)
+  int cntA = 0, cntB = 0;  // candidates staged (OWN: emitted) per query (wave-uniform)
 
   auto flush = [&](int which, int count) {
     __builtin_amdgcn_fence(__ATOMIC_ACQ_REL, "wavefront");
@@ -220,12 +223,19 @@ score_tile_kernel(ScoreArgs a) {
               const uint32_t mm = sel ? mB : mA;
               const int rank = __popc(mm & ((1u << (lane & 15)) - 1u));
               const int slot = (sel ? cntB : cntA) + rank;
-              stage[wave][sel][slot] = make_uint2((uint32_t)key, __float_as_uint(sc[cb]));
+              const uint2 c = make_uint2((uint32_t)key, __float_as_uint(sc[cb]));
+              if constexpr (OWN) {
+                if (slot < a.cap) a.cand[(int64_t)qs * a.cap + slot] = c;
+              } else {
+                stage[wave][sel][slot] = c;
+              }
             }
             cntA += __popc(mA);
             cntB += __popc(mB);
-            if (cntA > kSB - 16) { flush(0, cntA); cntA = 0; }
-            if (cntB > kSB - 16) { flush(1, cntB); cntB = 0; }
+            if constexpr (!OWN) {
+              if (cntA > kSB - 16) { flush(0, cntA); cntA = 0; }
+              if (cntB > kSB - 16) { flush(1, cntB); cntB = 0; }
+            }
           }
         }
       }
@@ -266,7 +276,13 @@ score_tile_kernel(ScoreArgs a) {
     if (it + 2 < ntiles) step(it + 2, t2, t1);
     if (it + 3 < ntiles) step(it + 3, t3, t2);
   }
-  if constexpr (!ROWS) {
+  if constexpr (!ROWS && OWN) {
+    // the total count, including candidates beyond cap (the check reads it)
+    if (lane == 0) {
+      if (qa >= 0) a.cnt[qa] = cntA;
+      if (qb >= 0) a.cnt[qb] = cntB;
+    }
+  } else if constexpr (!ROWS) {
     if (cntA > 0) flush(0, cntA);
     if (cntB > 0) flush(1, cntB);
   }
@@ -278,9 +294,11 @@ static hipError_t launch_rb(const ScoreArgs& a, hipStream_t s) {
   const int groups = (a.nq + gq - 1) / gq;
   dim3 grid((unsigned)(groups * a.nsplit)), block(Group<FMT>::THREADS);
   if (a.rows) {
-    hipLaunchKernelGGL((score_tile_kernel<RB, D, FMT, true>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((score_tile_kernel<RB, D, FMT, true, false>), grid, block, 0, s, a);
+  } else if (a.nsplit == 1) {
+    hipLaunchKernelGGL((score_tile_kernel<RB, D, FMT, false, true>), grid, block, 0, s, a);
   } else {
-    hipLaunchKernelGGL((score_tile_kernel<RB, D, FMT, false>), grid, block, 0, s, a);
+    hipLaunchKernelGGL((score_tile_kernel<RB, D, FMT, false, false>), grid, block, 0, s, a);
   }
   return hipGetLastError();
 }
