@@ -75,16 +75,24 @@ struct Span {
     std::lock_guard<std::mutex> g(t.mu);
     if (!t.on) return;
     a = take_event(t);
-    if (a) hipEventRecord(a, s);
+    if (a && hipEventRecord(a, s) != hipSuccess) {  // no timing for this span
+      (void)hipGetLastError();  // handled here; keep it from the next launch check
+      t.pool.push_back(a);
+      a = nullptr;
+    }
   }
   ~Span() {
     if (!a) return;
     Tracer& t = tracer();
     std::lock_guard<std::mutex> g(t.mu);
     hipEvent_t b = take_event(t);
-    if (!b) return;
-    hipEventRecord(b, s);
-    t.pending.push_back(TraceRec{name, a, b});
+    if (b && hipEventRecord(b, s) == hipSuccess) {
+      t.pending.push_back(TraceRec{name, a, b});
+      return;
+    }
+    if (b) (void)hipGetLastError();  // handled here; keep it from the next launch check
+    t.pool.push_back(a);  // the span is dropped; both events go back to the pool
+    if (b) t.pool.push_back(b);
   }
 };
 
