@@ -204,7 +204,7 @@ void splits(int64_t nq, int64_t maxctx, int fmt, int& nsplit, int& split_len) {
   const int64_t most = std::max<int64_t>(1, (maxctx + 4095) / 4096);
   want = std::max<int64_t>(1, std::min(want, most));
   int64_t len = (maxctx + want - 1) / want;
-  len = (len + 63) / 64 * 64;
+  len = (len + 127) / 128 * 128;  // whole key tiles
   nsplit = (int)((maxctx + len - 1) / len);
   split_len = (int)len;
 }

@@ -2,7 +2,7 @@
 //
 // A workgroup of 8 waves (4 for the scaled formats) owns 16 (8) queries, one
 // query pair per wave held in registers as MFMA A operands, and streams key
-// tiles of 64 keys through LDS; every key tile is read from memory once per
+// tiles of 128 keys through LDS; every key tile is read from memory once per
 // workgroup.
 // Per 16-key column block each wave runs 8 x 4 MFMAs (bf16, H = 64, d = 128),
 // applies ReLU and the weighted head sum in registers and then either
@@ -19,7 +19,7 @@
 
 namespace hk {
 
-constexpr int kTK = 64;          // keys per LDS stage
+constexpr int kTK = 64;          // keys per scoring pass (a stage holds two)
 // Waves per workgroup, one query pair each: 8 for bf16; 4 for the scaled
 // formats, whose epilogue outweighs their MFMAs -- two independent groups per
 // CU then drift out of phase and one group's epilogue overlaps the other's
@@ -56,8 +56,9 @@ score_tile_kernel(ScoreArgs a) {
   using F = Fmt<FMT>;
   using Frag = typename T::Frag;
   constexpr int RBYTES = T::RBYTES, NCH = T::NCH, KS = T::KS;
-  // keys per stage: 64, or 128 for 64-byte E2M1 rows (every stage is 8-16 KB)
-  constexpr int TK = FMT == kMXFP4 ? 2 * kTK : kTK;
+  // keys per stage: 128 (32 KB of bf16 rows, 16 KB of E4M3, 8 KB of E2M1),
+  // scored in passes of four 16-key column blocks
+  constexpr int TK = 2 * kTK;
   static_assert(!F::MX || KS == 1, "MX scales are loaded for one k-step");
   constexpr int TILE_BYTES = TK * RBYTES;
   constexpr int OPS = TILE_BYTES / (kThreads * 16);  // 16-byte DMA loads per lane per tile
@@ -166,17 +167,19 @@ score_tile_kernel(ScoreArgs a) {
     float f[NCB];
     int e[NCB];
   };
-  auto compute = [&](int it, const uint8_t* tb, const KeyScales& ksc) {
-    const int k0 = kb + it * TK;
-    float sc[NCB];
+  constexpr int NCP = NCB > 4 ? 4 : NCB;  // column blocks per scoring pass
+  auto compute_part = [&](int it, int part, const uint8_t* tb, const KeyScales& ksc) {
+    const int k0 = kb + it * TK + part * NCP * 16;
+    tb += part * NCP * 16 * RBYTES;
+    float sc[NCP];
 #pragma unroll
-    for (int cb = 0; cb < NCB; ++cb) {
+    for (int cb = 0; cb < NCP; ++cb) {
       const int kt = cb * 16 + (lane & 15);
       Frag b[KS];
       int sb[KS];
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
-        sb[ks] = F::MX ? ksc.e[cb] : 127;
+        sb[ks] = F::MX ? ksc.e[part * NCP + cb] : 127;
         // the chunks Fmt::frag names, at their swizzled places in the stage
         constexpr int CPS = F::SLICE / 16;  // chunks per k-step slice
         const uint8_t* krow = tb + kt * RBYTES;
@@ -192,27 +195,27 @@ score_tile_kernel(ScoreArgs a) {
         }
       }
       float s = qt.score(b, sb);
-      if constexpr (FMT == kFP8) s *= ksc.f[cb];
+      if constexpr (FMT == kFP8) s *= ksc.f[part * NCP + cb];
       sc[cb] = s;
     }
     if constexpr (ROWS) {
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
+      for (int cb = 0; cb < NCP; ++cb) {
         const int key = k0 + cb * 16 + (lane & 15);
         if (owner && key >= first && key < lim) a.rows[(int64_t)es * a.row_stride + key] = sc[cb];
       }
     } else {
-      // One uniform branch per tile: the candidate path runs only when some
-      // key of the tile passes (about one tile in three at 1M keys).
+      // One uniform branch per pass: the candidate path runs only when some
+      // key of the 64 passes (about one pass in two at the 1M shape).
       bool any = false;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
+      for (int cb = 0; cb < NCP; ++cb) {
         const int key = k0 + cb * 16 + (lane & 15);
         any |= owner && key >= first && key < lim && sc[cb] >= tau;
       }
       if (__ballot(any)) {
 #pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
+        for (int cb = 0; cb < NCP; ++cb) {
           const int key = k0 + cb * 16 + (lane & 15);
           const bool pass = owner && key >= first && key < lim && sc[cb] >= tau;
           const uint64_t m = __ballot(pass);
@@ -240,6 +243,11 @@ score_tile_kernel(ScoreArgs a) {
         }
       }
     }
+  };
+
+  auto compute = [&](int it, const uint8_t* tb, const KeyScales& ksc) {
+#pragma unroll
+    for (int part = 0; part < NCB / NCP; ++part) compute_part(it, part, tb, ksc);
   };
 
   // Per tile: wait for this wave's loads of tile `it`, barrier (every wave's
