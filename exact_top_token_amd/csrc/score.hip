@@ -113,15 +113,26 @@ score_tile_kernel(ScoreArgs a) {
   const int dma_kk = wave * KPB + lane / NCH;
   const int dma_c = ((lane % NCH) ^ (dma_kk & (NCH - 1))) * 16;
   const int full_tiles = (a.L - kb) / TK;  // tiles that lie entirely below L
+  // Full tiles (all but the last one or two) take a per-lane constant offset
+  // from a scalar tile base, and the LDS destination is wave-uniform, so
+  // issuing a tile costs almost no vector work.
+  const int wave_u = __builtin_amdgcn_readfirstlane(wave);
+  const int dma_off = dma_kk * RBYTES + dma_c;  // load p adds p * kWaves * 1 KB
   auto issue = [&](int tile, uint8_t* buf) {
     const int k0 = kb + tile * TK;
     const uint8_t* base = a.k + (int64_t)k0 * RBYTES;
+    if (tile < full_tiles) {  // uniform
 #pragma unroll
-    for (int p = 0; p < OPS; ++p) {
-      const int kk = dma_kk + p * kWaves * KPB;
-      int off = kk * RBYTES + dma_c;
-      if (tile >= full_tiles) off = (min(k0 + kk, a.L - 1) - k0) * RBYTES + dma_c;  // never past L
-      __builtin_amdgcn_global_load_lds(base + off, HK_LDS(buf + (p * kWaves + wave) * 1024), 16, 0, 0);
+      for (int p = 0; p < OPS; ++p)
+        __builtin_amdgcn_global_load_lds(base + (dma_off + p * kWaves * 1024),
+                                         HK_LDS(buf + (p * kWaves + wave_u) * 1024), 16, 0, 0);
+    } else {
+#pragma unroll
+      for (int p = 0; p < OPS; ++p) {
+        const int kk = dma_kk + p * kWaves * KPB;
+        const int off = (min(k0 + kk, a.L - 1) - k0) * RBYTES + dma_c;  // never past L
+        __builtin_amdgcn_global_load_lds(base + off, HK_LDS(buf + (p * kWaves + wave_u) * 1024), 16, 0, 0);
+      }
     }
   };
   issue(0, t0);
