@@ -19,7 +19,7 @@
 //     hold 32 heads of query A (heads 8rb + 4(g & 1) + i), lanes 32..63 the
 //     same heads of query B.
 // Epilogue: each lane sums w * max(acc, 0) over its 32 heads in a fixed order
-// (two partials, see epilogue()), then adds its partner lane (lane ^ 16).  A
+// (two partials, see score()), then adds its partner lane (lane ^ 16).  A
 // (query, key) score is bit-identical whichever kernel, tile position or query
 // pairing computed it.
 #pragma once
@@ -85,30 +85,24 @@ struct PairTile {
   // Scores of both queries against 16 keys whose B fragments are b[ks] (with
   // E8M0 scales sb[ks] for MX).  Returns this lane's score: query (lane < 32 ?
   // A : B), key (lane % 16), before the per-key FP8 scale.
-  __device__ __forceinline__ float score(const Frag (&b)[KS], const int (&sb)[KS]) const {
-    f32x4 acc[RB];
-#pragma unroll
-    for (int rb = 0; rb < RB; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int rb = 0; rb < RB; ++rb) acc[rb] = F::mma(a[rb][ks], b[ks], acc[rb], sa[rb][ks], sb[ks]);
-    }
-    return epilogue(acc);
-  }
-
+  //
   // Canonical head-sum order (every kernel that produces a score follows it):
   // per lane, one partial over the even row blocks and one over the odd row
   // blocks (row block ascending, register ascending), t = even + odd, then
   // t + t(lane ^ 16).  A tile holding one query per MFMA (16 heads per row
   // block) sees the same four partials in its four lane groups.
-  __device__ __forceinline__ float epilogue(const f32x4 (&acc)[RB]) const {
+  __device__ __forceinline__ float score(const Frag (&b)[KS], const int (&sb)[KS]) const {
+    // one row block at a time: its k-steps, then its share of the head sum
+    // (row blocks ascending, so the partials follow the canonical order)
     float se = 0.0f, so = 0.0f;
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) acc = F::mma(a[rb][ks], b[ks], acc, sa[rb][ks], sb[ks]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float r = __builtin_fmaxf(acc[rb][i], 0.0f);
+        const float r = __builtin_fmaxf(acc[i], 0.0f);
         if (rb & 1) {
           so = __builtin_fmaf(r, wf[rb][i], so);
         } else {
