@@ -84,19 +84,15 @@ struct QueryTile {
 
   // Score of (query, key lane % 16), in every lane, before the FP8 key scale.
   __device__ __forceinline__ float score(const Frag (&b)[KS], const int (&sb)[KS]) const {
-    f32x4 acc[RB4];
-#pragma unroll
-    for (int rb = 0; rb < RB4; ++rb) acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int ks = 0; ks < KS; ++ks) {
-#pragma unroll
-      for (int rb = 0; rb < RB4; ++rb) acc[rb] = F::mma(qa[rb][ks], b[ks], acc[rb], sa[rb][ks], sb[ks]);
-    }
+    // one row block at a time (row blocks ascending: the canonical order)
     float p = 0.0f;
 #pragma unroll
     for (int rb = 0; rb < RB4; ++rb) {
+      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p = __builtin_fmaf(__builtin_fmaxf(acc[rb][i], 0.0f), wf[rb][i], p);
+      for (int ks = 0; ks < KS; ++ks) acc = F::mma(qa[rb][ks], b[ks], acc, sa[rb][ks], sb[ks]);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) p = __builtin_fmaf(__builtin_fmaxf(acc[i], 0.0f), wf[rb][i], p);
     }
     const float t = p + __shfl_xor(p, 32);  // even + odd row blocks of this half
     return t + __shfl_xor(t, 16);           // + the other half
