@@ -40,8 +40,10 @@ constexpr int kSB = 128;         // staged candidates per query before a flush
 
 // Key tiles stream through four LDS stages filled by direct-to-LDS loads
 // (global_load_lds_dwordx4), three tiles ahead of the one being scored, with
-// one workgroup barrier per tile.  The stages are distinct LDS objects so the
-// compiler can tell the loads into one stage from reads of another.
+// one workgroup barrier per tile.  (The compiler cannot tell a stage being
+// refilled from the one being read and waits for every outstanding tile
+// load before a tile's first LDS read; the refills come from L2, so that
+// wait costs little.)
 // OWN (COMPACT with one key split): each wave is the only writer of its two
 // queries' candidates, so it keeps their counts in registers and every
 // passing lane stores its candidate straight to its slot; with several
