@@ -35,10 +35,17 @@ KERNEL_SOURCES = ["exact_top_token_amd/csrc/score.hip", "exact_top_token_amd/csr
 
 
 def kernel_hash() -> str:
+    """Hash of the score kernel's sources with comments and blank space
+    removed: stored HBM counters stay valid across comment-only edits and
+    become stale on any change to the code."""
+    import re
     h = hashlib.sha256()
     for rel in KERNEL_SOURCES:
-        with open(os.path.join(ROOT, rel), "rb") as f:
-            h.update(f.read())
+        with open(os.path.join(ROOT, rel), encoding="utf-8") as f:
+            src = f.read()
+        src = re.sub(r"/\*.*?\*/", " ", src, flags=re.S)
+        src = re.sub(r"//[^\n]*", " ", src)
+        h.update(" ".join(src.split()).encode())
     return h.hexdigest()[:16]
 
 
