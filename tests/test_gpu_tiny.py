@@ -127,6 +127,31 @@ def test_ragged_shapes_bit_exact(hk, L, n, H, d, k, seed):
     assert np.all(np.isneginf(_np(rep)[~ok]))
 
 
+def test_one_split_with_partial_last_group(hk):
+    """n = 8,190 queries fill 512 query groups, so the fused kernel runs one
+    key split per query (each wave the only writer of its queries'
+    candidates) and the last group holds 14 queries: its last wave has no
+    query.  Integer inputs: the selection equals the oracle bit for bit on 96
+    queries (the last 48 and 48 random ones) and the row baseline on all."""
+    L, n, H, d, k = 12000, 8190, 64, 128, 256
+    say(f"one split, partial last group: L={L} n={n} H={H} d={d} k={k}")
+    inp = datagen.make_custom("onesplit", L, n, H, d, k, dist="int", seed=11)
+    dv = to_device(inp)
+    idx, sc, st = hk.select(dv["q"], dv["k"], dv["w"], k, with_stats=True)
+    bidx, bsc = hk.baseline_select(dv["q"], dv["k"], dv["w"], k)
+    torch.cuda.synchronize()
+    assert st["n_failed"] == 0, st
+    assert np.array_equal(_np(idx), _np(bidx))
+    assert np.array_equal(_np(sc).view(np.uint32), _np(bsc).view(np.uint32))
+    qs = np.unique(np.concatenate([np.arange(n - 48, n),
+                                   np.random.default_rng(11).choice(n - 48, 48, replace=False)]))
+    rows = oracle_rows(inp, qs)
+    ref = [oracle.exact_topk(r, k) for r in rows]
+    for j, i in enumerate(qs):
+        assert np.array_equal(_np(idx)[i], ref[j][0]), f"query {i}"
+        assert np.array_equal(_np(sc)[i], ref[j][1].astype(np.float32)), f"query {i}"
+
+
 def test_explicit_q_start(hk):
     """Queries need not sit at the end: q_start + n < L."""
     say("q_start: L=2000 n=40 q_start=900")
