@@ -29,44 +29,20 @@ constexpr int kMaxRounds = 4;  // k <= 2048 = kMaxRounds * kSelThreads
 // ----------------------------------------------------------------- helpers
 
 struct SortScratch {
-  int cnt[256 * kSelWaves];  // per (digit, wave) counts, then offsets
+  int cnt[kSelWaves][256];  // per (wave, digit) running counts, then offsets
   int wsum[kSelWaves];
   int skip;
 };
-
-// Exclusive scan, in place, of `m` ints of `v` (m <= 4 * kSelThreads).
-__device__ void block_scan_excl(int* v, int m, int* wsum) {
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  int a[4];
-  int loc = 0;
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = 4 * tid + j;
-    a[j] = i < m ? v[i] : 0;
-    loc += a[j];
-  }
-  const int pre = wave_prefix_excl(loc);
-  if (lane == kWave - 1) wsum[wave] = pre + loc;
-  __syncthreads();
-  int base = pre;
-  for (int w = 0; w < wave; ++w) base += wsum[w];
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int i = 4 * tid + j;
-    if (i < m) v[i] = base;
-    base += a[j];
-  }
-  __syncthreads();
-}
 
 // Stable LSD radix sort, ascending by key bits [lo, hi), of the N <= 2048
 // (key, val) pairs in (k0, v0); (k1, v1) is scratch of the same size.
 // Digits are up to 8 bits wide (the passes split [lo, hi) evenly).  Wave w
 // ranks entries 256 w .. 256 w + 255 in four rounds of 64: the lanes holding
-// the same digit are found with one ballot per digit bit, and a per-(digit,
-// wave) running count in LDS carries the rank across rounds, so entries with
-// equal digits keep their order.  Returns true when the result ended in
-// (k1, v1).
+// the same digit are found with one ballot per digit bit, and a running
+// count per (wave, digit) in LDS (each wave its own row, so lanes with
+// different digits hit different banks) carries the rank across rounds, so
+// entries with equal digits keep their order.  Offsets follow (digit, wave)
+// order.  Returns true when the result ended in (k1, v1).
 __device__ __forceinline__ bool block_sort_pairs(uint32_t* k0, uint32_t* v0, uint32_t* k1, uint32_t* v1, int N,
                                  int lo, int hi, SortScratch& ss) {
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
@@ -78,9 +54,8 @@ __device__ __forceinline__ bool block_sort_pairs(uint32_t* k0, uint32_t* v0, uin
     const int w = (hi - sh + (passes - p) - 1) / (passes - p);  // digit bits of this pass
     const int nd = 1 << w;
     const uint32_t dmask = (uint32_t)nd - 1u;
-    for (int b = tid; b < nd * kSelWaves; b += kSelThreads) ss.cnt[b] = 0;
+    for (int b = lane; b < nd; b += kWave) ss.cnt[wave][b] = 0;  // this wave's row
     if (tid == 0) ss.skip = 0;
-    __syncthreads();
     uint32_t myd[kMaxRounds];
     int myrank[kMaxRounds];
 #pragma unroll
@@ -96,35 +71,47 @@ __device__ __forceinline__ bool block_sort_pairs(uint32_t* k0, uint32_t* v0, uin
       }
       int rank = 0;
       if (ok) {
-        const int before = ss.cnt[d * kSelWaves + wave];
+        const int before = ss.cnt[wave][d];
         rank = before + __popcll(m & lt);
         // the lowest lane of each digit group advances the running count
-        if ((m & lt) == 0ull) ss.cnt[d * kSelWaves + wave] = before + __popcll(m);
+        if ((m & lt) == 0ull) ss.cnt[wave][d] = before + __popcll(m);
       }
       myd[j] = d;
       myrank[j] = rank;
     }
     __syncthreads();
-    // A pass whose digit is the same for all N entries leaves the order alone.
-    for (int dd = tid; dd < nd; dd += kSelThreads) {
-      int tot = 0;
+    // digit totals, their exclusive scan (digits in threads 0..255), then the
+    // offset of each (digit, wave) in (digit, wave) order
+    int tot = 0, pre = 0;
+    if (tid < 256) {
+      if (tid < nd) {
 #pragma unroll
-      for (int v = 0; v < kSelWaves; ++v) tot += ss.cnt[dd * kSelWaves + v];
-      if (tot == N) ss.skip = 1;
+        for (int v = 0; v < kSelWaves; ++v) tot += ss.cnt[v][tid];
+      }
+      pre = wave_prefix_excl(tot);
+      if (lane == kWave - 1) ss.wsum[wave] = pre + tot;
+      if (tot == N) ss.skip = 1;  // one digit for all entries: order unchanged
     }
     __syncthreads();
     const bool skip = ss.skip != 0;
-    sh += w;
-    if (skip) {  // uniform
-      __syncthreads();  // everyone has read the flag before thread 0 resets it
-      continue;
+    if (!skip && tid < nd) {
+      int base = pre;
+      for (int v = 0; v < wave; ++v) base += ss.wsum[v];
+#pragma unroll
+      for (int v = 0; v < kSelWaves; ++v) {
+        const int c = ss.cnt[v][tid];
+        ss.cnt[v][tid] = base;
+        base += c;
+      }
     }
-    block_scan_excl(ss.cnt, nd * kSelWaves, ss.wsum);
+    __syncthreads();  // offsets ready; every thread has read the skip flag
+    sh += w;
+    if (skip) continue;  // uniform
 #pragma unroll
     for (int j = 0; j < kMaxRounds; ++j) {
       const int i = wave * (kMaxRounds * kWave) + j * kWave + lane;
       if (i < N) {
-        const int dst = ss.cnt[myd[j] * kSelWaves + wave] + myrank[j];
+        const int dst = ss.cnt[wave][myd[j]] + myrank[j];
         k1[dst] = k0[i];
         v1[dst] = v0[i];
       }
