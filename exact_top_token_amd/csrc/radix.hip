@@ -4,7 +4,7 @@
 // * check: a query fails when its candidates overflowed the buffer (count >
 //   cap) or number fewer than min(k, ctx).
 // * cand_select: for every query that passed, the exact top-k of its
-//   candidates.  Candidates arrive in whatever order the atomic flushes left
+//   candidates.  Candidates arrive in whatever order the scoring kernel left
 //   them, so every step below depends only on the candidate multiset, which
 //   makes the output bitwise reproducible:
 //     1. radix select of the k-th largest order-preserving score key;
