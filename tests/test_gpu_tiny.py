@@ -127,18 +127,24 @@ def test_ragged_shapes_bit_exact(hk, L, n, H, d, k, seed):
     assert np.all(np.isneginf(_np(rep)[~ok]))
 
 
-def test_one_split_with_partial_last_group(hk):
-    """n = 8,190 queries fill 512 query groups, so the fused kernel runs one
-    key split per query (each wave the only writer of its queries'
-    candidates) and the last group holds 14 queries: its last wave has no
-    query.  Integer inputs: the selection equals the oracle bit for bit on 96
-    queries (the last 48 and 48 random ones) and the row baseline on all."""
-    L, n, H, d, k = 12000, 8190, 64, 128, 256
-    say(f"one split, partial last group: L={L} n={n} H={H} d={d} k={k}")
-    inp = datagen.make_custom("onesplit", L, n, H, d, k, dist="int", seed=11)
+@pytest.mark.parametrize("fmt,L,n", [("bf16", 12000, 8190), ("mxfp8", 8000, 4094),
+                                     ("mxfp4", 8000, 4094)])
+def test_one_split_with_partial_last_group(hk, fmt, L, n):
+    """n queries fill 512 query groups (16 per group for bf16, 8 for the scaled
+    formats), so the fused kernel runs one key split per query -- each wave
+    the only writer of its queries' candidates -- and the last group is
+    partial: its last wave has no query.  Integer inputs (exact in every
+    format): the selection equals the oracle bit for bit on 96 queries (the
+    last 48 and 48 random ones) and the row baseline on all."""
+    H, d, k = 64, 128, 256
+    say(f"one split, partial last group: {fmt} L={L} n={n} H={H} d={d} k={k}")
+    inp = datagen.make_custom("onesplit", L, n, H, d, k, dtype=fmt, dist="int", seed=11)
     dv = to_device(inp)
-    idx, sc, st = hk.select(dv["q"], dv["k"], dv["w"], k, with_stats=True)
-    bidx, bsc = hk.baseline_select(dv["q"], dv["k"], dv["w"], k)
+    kw = {}
+    if fmt != "bf16":
+        kw = dict(q_scale=dv["q_scale"], k_scale=dv["k_scale"], fmt=fmt)
+    idx, sc, st = hk.select(dv["q"], dv["k"], dv["w"], k, with_stats=True, **kw)
+    bidx, bsc = hk.baseline_select(dv["q"], dv["k"], dv["w"], k, **kw)
     torch.cuda.synchronize()
     assert st["n_failed"] == 0, st
     assert np.array_equal(_np(idx), _np(bidx))
