@@ -418,7 +418,7 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
                                     r.cap, (int)p->L, out_idx, out_score, s),
              "candidate select launch");
     }
-    // Recovery: rescore only the flagged queries over their whole context.
+    // Recovery: full score rows for the flagged queries only, then row top-k.
     for (int f0 = 0; f0 < hs.n_failed; f0 += l.rows_n) {
       const int nf = std::min(l.rows_n, hs.n_failed - f0);
       rc = rows_path(p, base, failed + f0, 0, nf, maxctx, rows, out_idx, out_score, s);

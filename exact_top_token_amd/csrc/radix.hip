@@ -12,7 +12,7 @@
 //        ties (the pages break ties at the k-th score by position, with a
 //        radix select);
 //     3. LSD radix sort of the kept k by (score descending, position
-//        ascending) (the pages order the kept entries with a radix sort).
+//        ascending) (the pages sort the k survivors by radix).
 // * row_topk: the same result from materialised score rows (the conventional
 //   two-kernel route, recovery and full rescore): radix select over the row,
 //   emission of the kept entries in position order (ties: first ones win),

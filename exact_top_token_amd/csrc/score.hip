@@ -6,7 +6,7 @@
 // workgroup.
 // Per 16-key column block each wave runs 8 x 4 MFMAs (bf16, H = 64, d = 128),
 // applies ReLU and the weighted head sum in registers and then either
-//   COMPACT: compares each score with the query's sampled threshold in
+//   COMPACT: tests every score against the query's sampled threshold in
 //     registers and emits only the passing keys into the query's bounded
 //     candidate buffer, so no score table is written (HyScale explainer,
 //     HyTopK paragraph);

@@ -3,11 +3,11 @@
  * Instinct MI355X (gfx950).
  *
  * Operation (HyScale pages):
- *   * Learned sparse attention scores every earlier token of each query with
- *     an indexer and keeps the k best; the conventional route writes the full
- *     query x key score table to GPU memory and a second kernel reads it back
- *     for top-k ("HyScale sparse-attention training -- Selection without a
- *     score table", contest paragraph).
+ *   * Learned sparse attention rates all of a query's preceding tokens with
+ *     an indexer and keeps the k best; done conventionally, the complete
+ *     query x key table of scores lands in device memory and a separate
+ *     top-k pass loads it again ("HyScale sparse-attention training --
+ *     Selection without a score table", contest paragraph).
  *   * HyTopK (also called FlashTopK) returns each query's exact top-k without
  *     that table: a threshold taken from evenly spaced samples of the query's
  *     own context, a fused score-and-compare pass that writes only passing keys
@@ -97,7 +97,7 @@ typedef enum {
  * back in one key buffer); query i then sees keys q_first[i] .. q_pos[i].
  * Values are clamped to [0, L); a query whose range is empty gets only
  * padding.  The sample count M is taken from L, the keys of the call; the
- * sample positions and the threshold rank from the query's own context.
+ * sample positions and the threshold rank from that query's context alone.
  * Replay and backward take explicit indices and ignore both arrays. */
 typedef struct {
   int64_t L;        /* number of keys */
@@ -172,7 +172,7 @@ int hytopk_replay(const hytopk_problem* p, const void* q, const void* q_scale,
                   float* out_score, void* stream);
 
 /* The conventional route: write the n x L fp32 score table into the
- * workspace, then a row top-k kernel reads it back.  Same outputs as
+ * workspace, then a row top-k over the table.  Same outputs as
  * hytopk_select. */
 int hytopk_baseline_select(const hytopk_problem* p, const void* q, const void* q_scale,
                            const void* k, const void* k_scale, const float* w,

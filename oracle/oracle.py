@@ -20,8 +20,8 @@ Sources, cited by page title and passage:
   Summary's *Original abstract* section).
 
 What this oracle computes is the plain definition, because the method reaches
-exactly that result [Abstract: HyTopK finds each query's exact top-k without a
-score table]:
+exactly that result ([Abstract]: HyTopK returns the exact top-k of every
+query without materialising a table of scores):
 
 1. decode the stored inputs exactly to fp64 (bf16 bits; OCP E4M3 codes times
    their per-token fp32 scales; OCP MX block-scaled E4M3 / E2M1 elements times
@@ -375,7 +375,7 @@ def sample_count(L: int, m_min: int = 4096, m_max: int = 8192, m_div: int = 128)
 
 
 def sample_positions(ctx: int, M: int) -> np.ndarray:
-    """Evenly spaced samples from the query's own context [Explainer, HyTopK]:
+    """Evenly spaced samples of that query's context [Explainer, HyTopK]:
     M_q = min(M, ctx) positions floor(j * ctx / M_q), j = 0..M_q-1."""
     mq = min(M, ctx)
     j = np.arange(mq, dtype=np.int64)
