@@ -48,6 +48,13 @@ struct Fmt {
     }
   }
 
+  // D += A x B where A is E4M3 (the linear row block) and B this format.
+  __device__ __forceinline__ static f32x4 mma_lin(const i32x8& a, const Frag& b, const f32x4& c,
+                                                  int sa, int sb) {
+    static_assert(SCALED, "bf16 has no linear row block");
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, CODE, 0, sa, 0, sb);
+  }
+
   // Bytes of one k-step slice of a row (KMMA elements).
   static constexpr int SLICE = KMMA * BITS / 8;
 

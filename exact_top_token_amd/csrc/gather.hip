@@ -40,10 +40,27 @@ struct QueryTile {
   Frag qa[RB4][KS];
   int sa[RB4][KS];
   float wf[RB4][4];
+  i32x8 lin;  // scaled formats: the linear row block (pieces of v in rows 0..5)
+  int lsa;
 
+  // lds: this wave's kLinWords dwords of LDS (16-byte aligned) for the linear
+  // row block of the scaled formats; unused for bf16.
   __device__ __forceinline__ void load(const uint8_t* q, const float* w, const void* q_scale, int H,
-                                       int qi) {
+                                       int qi, uint32_t* lds) {
     const int lane = lane_id(), r = lane & 15, g = lane >> 4;
+    if constexpr (F::SCALED) {
+      static_assert(KS == 1, "the linear row block covers one k-step");
+      // two elements of v per lane (the pair tile takes four per lane of a
+      // half wave; every element's arithmetic is the same either way)
+      float v[2];
+      uint32_t code[kLinPieces];
+      int scale[kLinPieces];
+      lin_v<FMT, D, 2>(q, w, q_scale, H, qi, 2 * lane, v);
+      lin_split<2, 64>(v, code, scale);
+      lin_store<2>(lds, lane, code, scale);
+      wave_lds_sync();
+      lin_frag<FMT>(lds, r, g, lin, lsa);
+    }
     float qs = 1.0f;
     if constexpr (FMT == kFP8) qs = static_cast<const float*>(q_scale)[qi];
 #pragma unroll
@@ -62,7 +79,7 @@ struct QueryTile {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int hw = 16 * rb + 4 * g + i;
-        wf[rb][i] = hw < H ? w[(int64_t)qi * H + hw] * qs : 0.0f;
+        wf[rb][i] = hw < H ? w[(int64_t)qi * H + hw] * qs * (F::SCALED ? 0.5f : 1.0f) : 0.0f;
       }
     }
   }
@@ -84,15 +101,24 @@ struct QueryTile {
 
   // Score of (query, key lane % 16), in every lane, before the FP8 key scale.
   __device__ __forceinline__ float score(const Frag (&b)[KS], const int (&sb)[KS]) const {
-    // one row block at a time (row blocks ascending: the canonical order)
+    // one row block at a time (row blocks ascending: the canonical order);
+    // for the scaled formats lane groups 0 and 1 start from their rows of the
+    // linear term (pieces 0..3 and 4, 5), groups 2 and 3 from zero rows
     float p = 0.0f;
+    if constexpr (F::SCALED) {
+      const f32x4 l = F::mma_lin(lin, b[0], f32x4{0.f, 0.f, 0.f, 0.f}, lsa, sb[0]);
+      p = (l[0] + l[1]) + (l[2] + l[3]);
+    }
 #pragma unroll
     for (int rb = 0; rb < RB4; ++rb) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) acc = F::mma(qa[rb][ks], b[ks], acc, sa[rb][ks], sb[ks]);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) p = __builtin_fmaf(__builtin_fmaxf(acc[i], 0.0f), wf[rb][i], p);
+      for (int i = 0; i < 4; ++i) {
+        const float x = F::SCALED ? __builtin_fabsf(acc[i]) : __builtin_fmaxf(acc[i], 0.0f);
+        p = __builtin_fmaf(x, wf[rb][i], p);
+      }
     }
     const float t = p + __shfl_xor(p, 32);  // even + odd row blocks of this half
     return t + __shfl_xor(t, 16);           // + the other half
@@ -107,12 +133,13 @@ __global__ void __launch_bounds__(kReplayThreads) replay_kernel(ReplayArgs a) {
   using Frag = typename T::Frag;
   constexpr int KS = T::KS;
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  __shared__ __attribute__((aligned(16))) uint32_t lin_lds[kReplayThreads / kWave][kLinWords];
   const int q = blockIdx.x * (kReplayThreads / kWave) + wave;
   if (q >= a.n) return;  // wave-uniform; no workgroup barrier in this kernel
   const int K = a.topk;
 
   T qt;
-  qt.load(a.q, a.w, a.q_scale, a.H, q);
+  qt.load(a.q, a.w, a.q_scale, a.H, q, lin_lds[wave]);
 
   const int* ids = a.idx + (int64_t)q * K;
   float* out = a.out + (int64_t)q * K;
@@ -190,6 +217,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_tau_kernel(SampleArgs a
   constexpr int KS = T::KS;
   extern __shared__ float S[];  // sample scores, M_q entries
   __shared__ RadixScratch sc;
+  __shared__ __attribute__((aligned(16))) uint32_t lin_lds[kSampleThreads / kWave][kLinWords];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   // Workgroups are dispatched to the 8 XCDs round-robin; each XCD takes a
@@ -212,7 +240,7 @@ __global__ void __launch_bounds__(kSampleThreads) sample_tau_kernel(SampleArgs a
   r = max(1, min(mq, r));
 
   T qt;
-  qt.load(a.q, a.w, a.q_scale, a.H, q);
+  qt.load(a.q, a.w, a.q_scale, a.H, q, lin_lds[wave]);
 
   for (int cb = wave; cb * 16 < mq; cb += kSampleThreads / kWave) {
     const int j = cb * 16 + (lane & 15);

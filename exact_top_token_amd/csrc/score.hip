@@ -141,8 +141,13 @@ score_tile_kernel(ScoreArgs a) {
   if (1 < ntiles) issue(1, t1);
   if (2 < ntiles) issue(2, t2);
 
+  // The scaled formats build their linear row block in stage t3, which the
+  // first refill (after the first tile barrier) overwrites; the barrier here
+  // also waits for every wave's reads of it.
+  static_assert(!F::SCALED || kWaves * 2 * kLinWords * 4 <= TILE_BYTES, "t3 holds the pieces");
   T qt;
-  qt.load(a.q, a.w, a.q_scale, a.H, qa, qb);
+  qt.load(a.q, a.w, a.q_scale, a.H, qa, qb, reinterpret_cast<uint32_t*>(t3) + wave * 2 * kLinWords);
+  if constexpr (F::SCALED) __syncthreads();
 
   // This lane's query (lanes 0..31: A, 32..63: B) and its key limit.
   const int sel = lane >> 5;

@@ -22,11 +22,187 @@
 // (two partials, see score()), then adds its partner lane (lane ^ 16).  A
 // (query, key) score is bit-identical whichever kernel, tile position or query
 // pairing computed it.
+//
+// The scaled formats (FP8, MXFP8, MXFP4) take the weighted ReLU apart as
+// w * ReLU(x) = (w/2) * |x| + (w/2) * x.  Summed over the heads, the second
+// part is a single dot product v . k with v = sum_h (w_h / 2) q_h, which one
+// more MFMA row block computes; the per-head work left for the vector ALUs is
+// one fma with |acc| (an input modifier) instead of a max and an fma.  On
+// these formats the epilogue, not the MFMAs, bounds the kernel, so this takes
+// about an eighth off the scoring time (bf16 keeps max + fma: there the extra
+// row block costs as much as it saves and its registers do not fit).  v is
+// fp32; the MFMA operand carries it as kLinPieces E4M3 rows with one E8M0
+// scale each, piece j being the rounding of what pieces 0..j-1 left over (see
+// lin_split), so that the pieces sum to v within 2^-24 of its largest element
+// and exactly whenever v has fewer significant bits than that.
 #pragma once
 
 #include "common.h"
 
 namespace hk {
+
+// ------------------------------------------------------------ linear term
+
+constexpr int kLinPieces = 6;   // E4M3 pieces of v (about 4 bits each)
+constexpr int kLinWords = 200;  // LDS dwords per query: 32 per piece, the scales, padding
+
+// Element decoders.  fp32 denormals are kept (the kernels' float mode), so
+// a code's exponent and mantissa bits placed at the top of an fp32 mantissa
+// and scaled by a power of two give its value, subnormal codes included.
+// Finite OCP FP8 E4M3 code in bits 24..31 of t -> value (bias 7).
+__device__ __forceinline__ float e4m3_top(uint32_t t) {
+  return __uint_as_float((t & 0x80000000u) | ((t >> 4) & 0x07F00000u)) * 0x1p120f;
+}
+
+// OCP FP4 E2M1 code in bits 28..31 of t -> value (bias 1).
+__device__ __forceinline__ float e2m1_top(uint32_t t) {
+  return __uint_as_float((t & 0x80000000u) | ((t >> 6) & 0x01C00000u)) * 0x1p126f;
+}
+
+// E8M0 scale byte (< 255) -> 2^(s - 127).
+__device__ __forceinline__ float e8m0_value(uint32_t s) {
+  return s ? __uint_as_float(s << 23) : 0x1p-127f;
+}
+
+// E4M3 byte of a value that E4M3 holds exactly (|p| <= 448).
+__device__ __forceinline__ uint32_t e4m3_code(float p) {
+  const uint32_t u = __float_as_uint(p), a = u & 0x7FFFFFFFu;
+  const float m = __uint_as_float(a);
+  const uint32_t mag = m >= 0x1p-6f ? ((((a >> 23) - 120u) << 3) | ((a >> 20) & 7u))
+                                    : (uint32_t)(m * 512.0f);
+  return ((u >> 24) & 0x80u) | mag;
+}
+
+// NE consecutive elements d0 .. d0 + NE - 1 of v = sum_h (w_h q_scale / 2) q_h
+// for query qi (qi < 0: zeros), heads in ascending order, each element its
+// own fma chain (so any split of the elements over lanes gives the same
+// bits).  The head weights are formed exactly as the tiles form theirs; MX
+// elements are decoded with their block's scale.
+template <int FMT, int D, int NE>
+__device__ __forceinline__ void lin_v(const uint8_t* __restrict__ q, const float* __restrict__ w,
+                                      const void* __restrict__ q_scale, int H, int qi, int d0,
+                                      float (&v)[NE]) {
+  using F = Fmt<FMT>;
+  constexpr int RBYTES = D * F::BITS / 8;
+  static_assert(NE == 2 || NE == 4, "two or four elements per lane");
+#pragma unroll
+  for (int i = 0; i < NE; ++i) v[i] = 0.0f;
+  if (qi < 0) return;
+  float qs = 1.0f;
+  if constexpr (FMT == kFP8) qs = static_cast<const float*>(q_scale)[qi];
+#pragma unroll 4
+  for (int h = 0; h < H; ++h) {
+    const int64_t hr = (int64_t)qi * H + h;
+    const float hw = w[hr] * qs * 0.5f;
+    const uint8_t* row = q + hr * RBYTES;
+    float e[NE];
+    if constexpr (FMT == kMXFP4) {  // element 2i in the low nibble of byte i
+      const uint32_t x = NE == 4 ? *reinterpret_cast<const uint16_t*>(row + d0 / 2) : row[d0 / 2];
+#pragma unroll
+      for (int i = 0; i < NE; ++i) e[i] = e2m1_top(x << (28 - 4 * i));
+    } else {
+      const uint32_t x = NE == 4 ? *reinterpret_cast<const uint32_t*>(row + d0)
+                                 : *reinterpret_cast<const uint16_t*>(row + d0);
+#pragma unroll
+      for (int i = 0; i < NE; ++i) e[i] = e4m3_top(x << (24 - 8 * i));
+    }
+    if constexpr (F::MX) {
+      const float sc = e8m0_value(static_cast<const uint8_t*>(q_scale)[hr * (D / 32) + d0 / 32]);
+#pragma unroll
+      for (int i = 0; i < NE; ++i) e[i] *= sc;
+    }
+#pragma unroll
+    for (int i = 0; i < NE; ++i) v[i] = __builtin_fmaf(hw, e[i], v[i]);
+  }
+}
+
+// Splits v into kLinPieces E4M3 pieces: NE elements per lane, one query per
+// LANES consecutive lanes (32: a half wave, 64: the whole wave).  code[j]
+// packs this lane's codes of piece j (element i in byte i); scale[j] is piece
+// j's E8M0 scale byte, the same in all the query's lanes.  Piece j's scale
+// 2^e puts the largest remaining magnitude m in [128, 256) (e = floor(log2 m)
+// - 7, at least -127); each element is rounded to E4M3 at that scale (ties to
+// even: 4 significant bits, or steps of 2^-9 in the subnormal range) and the
+// exact rounding error is what piece j + 1 splits.
+template <int NE, int LANES>
+__device__ __forceinline__ void lin_split(const float (&v)[NE], uint32_t (&code)[kLinPieces],
+                                          int (&scale)[kLinPieces]) {
+  float res[NE];
+#pragma unroll
+  for (int i = 0; i < NE; ++i) res[i] = v[i];
+#pragma unroll
+  for (int j = 0; j < kLinPieces; ++j) {
+    float m = __builtin_fabsf(res[0]);
+#pragma unroll
+    for (int i = 1; i < NE; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(res[i]));
+#pragma unroll
+    for (int off = 1; off < LANES; off <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
+    const int e = max((int)((__float_as_uint(m) >> 23) & 0xFFu) - 134, -127);  // <= 120
+    scale[j] = e + 127;
+    const float down = __uint_as_float((uint32_t)(127 - e) << 23);               // 2^-e
+    const float up = e >= -126 ? __uint_as_float((uint32_t)(127 + e) << 23) : 0x1p-127f;
+    uint32_t c = 0;
+#pragma unroll
+    for (int i = 0; i < NE; ++i) {
+      const float x = res[i] * down;  // |x| < 256
+      const int ex = max((int)((__float_as_uint(x) >> 23) & 0xFFu) - 127, -6);
+      // x + 1.5 * 2^(ex + 20) has unit 2^(ex - 3): adding and removing it
+      // rounds x to E4M3's step at x's binade
+      const float magic = __uint_as_float(((uint32_t)(ex + 147) << 23) | 0x400000u);
+      const float p = (x + magic) - magic;
+      res[i] -= p * up;  // exact
+      c |= e4m3_code(p) << (8 * i);
+    }
+    code[j] = c;
+  }
+}
+
+// Publishes this lane's pieces (NE codes each, elements NE * l ..) in LDS
+// region `reg` (kLinWords dwords, 16-byte aligned; piece j's element d is
+// byte 128 j + d), l being the lane's index among its query's lanes.
+template <int NE>
+__device__ __forceinline__ void lin_store(uint32_t* reg, int l, const uint32_t (&code)[kLinPieces],
+                                          const int (&scale)[kLinPieces]) {
+#pragma unroll
+  for (int j = 0; j < kLinPieces; ++j) {
+    if constexpr (NE == 4) {
+      reg[32 * j + l] = code[j];
+    } else {
+      reinterpret_cast<uint16_t*>(reg + 32 * j)[l] = (uint16_t)code[j];
+    }
+  }
+  if (l < kLinPieces) {
+    int s = scale[0];
+#pragma unroll
+    for (int j = 1; j < kLinPieces; ++j) s = l == j ? scale[j] : s;
+    reg[32 * kLinPieces + l] = s;
+  }
+}
+
+// The linear row block's A fragment of lane group g holding piece j of the
+// query in `reg` (j >= kLinPieces: a zero row), in the chunk order of the
+// format's k-step (E4M3 elements d 32g .. 32g + 31 for per-token FP8, d 16g ..
+// 16g + 15 and 64 + 16g .. 64 + 16g + 15 for the MX order), and its scale.
+template <int FMT>
+__device__ __forceinline__ void lin_frag(const uint32_t* reg, int j, int g, i32x8& a, int& sa) {
+  a = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
+  sa = 127;
+  if (j < kLinPieces) {
+    const uint32_t* p = reg + 32 * j;
+    const int o0 = FMT == kFP8 ? 8 * g : 4 * g, o1 = FMT == kFP8 ? 8 * g + 4 : 16 + 4 * g;
+    const u32x4 lo = *reinterpret_cast<const u32x4*>(p + o0);
+    const u32x4 hi = *reinterpret_cast<const u32x4*>(p + o1);
+    a = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    sa = (int)reg[32 * kLinPieces + j];
+  }
+}
+
+// Orders this wave's LDS writes before its later LDS reads.
+__device__ __forceinline__ void wave_lds_sync() {
+  __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+  __builtin_amdgcn_wave_barrier();
+  __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+}
 
 template <int RB, int D, int FMT>
 struct PairTile {
@@ -42,13 +218,31 @@ struct PairTile {
 
   Frag a[RB][KS];   // query pair, A operand
   int sa[RB][KS];   // E8M0 scale of each A fragment's block (MX; 127 otherwise)
-  float wf[RB][4];  // head weights of this lane's 32 heads (times q_scale for FP8)
+  float wf[RB][4];  // head weights of this lane's 32 heads (times q_scale for FP8; halved
+                    // for the scaled formats)
+  i32x8 lin;        // scaled formats: the linear row block (pieces of v, rows 0..5: A, 8..13: B)
+  int lsa;          // its E8M0 scale
 
   // Load the A operand and weights of query indices qa / qb (-1 = absent).
-  // q_scale: fp32 [n] (FP8) or E8M0 bytes [n][H][D/32] (MX).
+  // q_scale: fp32 [n] (FP8) or E8M0 bytes [n][H][D/32] (MX).  lds: this
+  // wave's 2 * kLinWords dwords of LDS (16-byte aligned) for building the
+  // linear row block of the scaled formats; unused for bf16.
   __device__ __forceinline__ void load(const uint8_t* __restrict__ q, const float* __restrict__ w,
-                                       const void* __restrict__ q_scale, int H, int qa, int qb) {
+                                       const void* __restrict__ q_scale, int H, int qa, int qb,
+                                       uint32_t* lds) {
     const int lane = lane_id();
+    if constexpr (F::SCALED) {
+      static_assert(KS == 1, "the linear row block covers one k-step");
+      float v[4];
+      uint32_t code[kLinPieces];
+      int scale[kLinPieces];
+      lin_v<FMT, D, 4>(q, w, q_scale, H, (lane >> 5) ? qb : qa, 4 * (lane & 31), v);
+      lin_split<4, 32>(v, code, scale);
+      lin_store<4>(lds + (lane >> 5) * kLinWords, lane & 31, code, scale);
+      wave_lds_sync();
+      const int r = lane & 15;
+      lin_frag<FMT>(lds + (r >> 3) * kLinWords, r & 7, lane >> 4, lin, lsa);
+    }
     const int r = lane & 15, g = lane >> 4;
     const int qrow = (r >> 3) ? qb : qa;
 #pragma unroll
@@ -77,7 +271,7 @@ struct PairTile {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
         const int h = 8 * rb + hb + i;
-        wf[rb][i] = (qw >= 0 && h < H) ? w[(int64_t)qw * H + h] * qs : 0.0f;
+        wf[rb][i] = (qw >= 0 && h < H) ? w[(int64_t)qw * H + h] * qs * (F::SCALED ? 0.5f : 1.0f) : 0.0f;
       }
     }
   }
@@ -89,12 +283,20 @@ struct PairTile {
   // Canonical head-sum order (every kernel that produces a score follows it):
   // per lane, one partial over the even row blocks and one over the odd row
   // blocks (row block ascending, register ascending), t = even + odd, then
-  // t + t(lane ^ 16).  A tile holding one query per MFMA (16 heads per row
-  // block) sees the same four partials in its four lane groups.
+  // t + t(lane ^ 16).  For the scaled formats the even partial starts from
+  // the lane's share of the linear term, (l0 + l1) + (l2 + l3) over its four
+  // rows of the linear row block (pieces 0..3 in lane group 0, pieces 4, 5 in
+  // lane group 1), and the heads contribute (w/2) * |acc|.  A tile holding
+  // one query per MFMA (16 heads per row block) sees the same four partials
+  // in its four lane groups.
   __device__ __forceinline__ float score(const Frag (&b)[KS], const int (&sb)[KS]) const {
     // one row block at a time: its k-steps, then its share of the head sum
     // (row blocks ascending, so the partials follow the canonical order)
     float se = 0.0f, so = 0.0f;
+    if constexpr (F::SCALED) {
+      const f32x4 l = F::mma_lin(lin, b[0], f32x4{0.f, 0.f, 0.f, 0.f}, lsa, sb[0]);
+      se = (l[0] + l[1]) + (l[2] + l[3]);
+    }
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
       f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
@@ -102,7 +304,7 @@ struct PairTile {
       for (int ks = 0; ks < KS; ++ks) acc = F::mma(a[rb][ks], b[ks], acc, sa[rb][ks], sb[ks]);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float r = __builtin_fmaxf(acc[i], 0.0f);
+        const float r = F::SCALED ? __builtin_fabsf(acc[i]) : __builtin_fmaxf(acc[i], 0.0f);
         if (rb & 1) {
           so = __builtin_fmaf(r, wf[rb][i], so);
         } else {
