@@ -28,9 +28,9 @@
 // part is a single dot product v . k with v = sum_h (w_h / 2) q_h, which one
 // more MFMA row block computes; the per-head work left for the vector ALUs is
 // one fma with |acc| (an input modifier) instead of a max and an fma.  On
-// these formats the epilogue, not the MFMAs, bounds the kernel, so this takes
-// about an eighth off the scoring time (bf16 keeps max + fma: there the extra
-// row block costs as much as it saves and its registers do not fit).  v is
+// these formats the epilogue costs about as much as the MFMAs, and this takes
+// 4-5% off the scoring time at the 1M shape (bf16 keeps max + fma: there the
+// extra row block costs more than it saves and its registers do not fit).  v is
 // fp32; the MFMA operand carries it as kLinPieces E4M3 rows with one E8M0
 // scale each, piece j being the rounding of what pieces 0..j-1 left over (see
 // lin_split), so that the pieces sum to v within 2^-24 of its largest element
