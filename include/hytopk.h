@@ -181,7 +181,8 @@ int hytopk_baseline_select(const hytopk_problem* p, const void* q, const void* q
 
 /* Workspace bytes of hytopk_backward (0 on invalid input): the dk rows of one
  * chunk of queries plus the buffers that group them by key.  The chunk size
- * depends only on the problem (about 2 GiB of rows), so results do not depend
+ * depends only on the problem (up to 8 GiB of rows, d * 4 bytes per entry
+ * with k padded to an even number of 32-key tiles), so results do not depend
  * on the workspace a caller passes. */
 size_t hytopk_backward_workspace(const hytopk_problem* p);
 
