@@ -1,6 +1,6 @@
 // Fused indexer scoring over causal key ranges (the hot loop of HyTopK).
 //
-// A workgroup of 8 waves (4 for the scaled formats) owns 16 (8) queries, one
+// A workgroup of 8 waves (4 for MXFP4) owns 16 (8) queries, one
 // query pair per wave held in registers as MFMA A operands, and streams key
 // tiles of 128 keys through LDS; every key tile is read from memory once per
 // workgroup.
@@ -20,14 +20,16 @@
 namespace hk {
 
 constexpr int kTK = 64;          // keys per scoring pass (a stage holds two)
-// Waves per workgroup, one query pair each: 8 for bf16; 4 for the scaled
-// formats, whose epilogue outweighs their MFMAs -- two independent groups per
-// CU then drift out of phase and one group's epilogue overlaps the other's
-// MFMAs (measured at the 1M shape: FP8 -3%, MXFP8 -8%, MXFP4 -4% time; bf16
-// +4.5%, so it keeps one group of 8).
+// Waves per workgroup, one query pair each: 8 (one group per CU, 16 queries
+// sharing each key tile) except for MXFP4, which keeps 4: its registers
+// allow three waves per SIMD, so three independent groups of 4 share a CU
+// and drift out of phase, one group's epilogue overlapping another's MFMAs.
+// Measured at the 1M shape: 8 waves take FP8 and MXFP8 2.7-2.8% under 4 (with
+// the linear row block; before it, 4 were faster), MXFP4 is 0.9% slower with
+// 8, and bf16 4.5% slower with 4.
 template <int FMT>
 struct Group {
-  static constexpr int WAVES = FMT == kBF16 ? 8 : 4;
+  static constexpr int WAVES = FMT == kMXFP4 ? 4 : 8;
   static constexpr int THREADS = 64 * WAVES;
   static constexpr int QUERIES = 2 * WAVES;
 };
@@ -73,6 +75,8 @@ score_tile_kernel(ScoreArgs a) {
   __shared__ __attribute__((aligned(1024))) uint8_t t2[TILE_BYTES];
   __shared__ __attribute__((aligned(1024))) uint8_t t3[TILE_BYTES];
   __shared__ uint2 stage[(ROWS || OWN) ? 1 : kWaves][2][(ROWS || OWN) ? 1 : kSB];
+  // per wave: the pieces of its two queries' linear row blocks (scaled formats)
+  __shared__ __attribute__((aligned(16))) uint32_t lin_lds[F::SCALED ? kWaves : 1][2 * kLinWords];
   __shared__ int s_maxt[kWaves];
   __shared__ int s_minlo[kWaves];
 
@@ -141,13 +145,8 @@ score_tile_kernel(ScoreArgs a) {
   if (1 < ntiles) issue(1, t1);
   if (2 < ntiles) issue(2, t2);
 
-  // The scaled formats build their linear row block in stage t3, which the
-  // first refill (after the first tile barrier) overwrites; the barrier here
-  // also waits for every wave's reads of it.
-  static_assert(!F::SCALED || kWaves * 2 * kLinWords * 4 <= TILE_BYTES, "t3 holds the pieces");
   T qt;
-  qt.load(a.q, a.w, a.q_scale, a.H, qa, qb, reinterpret_cast<uint32_t*>(t3) + wave * 2 * kLinWords);
-  if constexpr (F::SCALED) __syncthreads();
+  qt.load(a.q, a.w, a.q_scale, a.H, qa, qb, lin_lds[F::SCALED ? wave : 0]);
 
   // This lane's query (lanes 0..31: A, 32..63: B) and its key limit.
   const int sel = lane >> 5;
@@ -350,7 +349,10 @@ hipError_t launch_score(const ScoreArgs& a, int d, int fmt, hipStream_t s) {
 }
 
 int score_group_queries(int fmt) {
-  return fmt == kBF16 ? Group<kBF16>::QUERIES : Group<kFP8>::QUERIES;
+  if (fmt == kFP8) return Group<kFP8>::QUERIES;
+  if (fmt == kMXFP8) return Group<kMXFP8>::QUERIES;
+  if (fmt == kMXFP4) return Group<kMXFP4>::QUERIES;
+  return Group<kBF16>::QUERIES;
 }
 
 }  // namespace hk
