@@ -60,3 +60,27 @@ def test_fp8_exact_every_path_bit_exact(hk, H, seed):
     torch.cuda.synchronize()
     assert np.array_equal(_np(rep).view(np.uint32), bits[1])
     assert np.array_equal(_np(bi), bits[0]) and np.array_equal(_np(bs).view(np.uint32), bits[1])
+
+
+def test_fp8_exact_one_split_partial_last_group(hk):
+    """8,190 queries fill 512 groups of 16, so the fused kernel runs one key
+    split per query (each wave the only writer of its candidates) and the
+    last group's last wave has no query; exact FP8 values: the selection
+    equals the row baseline on all queries and the oracle on 96 of them."""
+    L, n, H, k = 12000, 8190, 64, 256
+    say(f"fp8: exact problem, one split, L={L} n={n} H={H} d=128 k={k}")
+    inp = _fp8_exact(L, n, H, k, 97)
+    dv = to_device(inp)
+    kw = dict(q_scale=dv["q_scale"], k_scale=dv["k_scale"], fmt="fp8")
+    idx, sc, st = hk.select(dv["q"], dv["k"], dv["w"], k, with_stats=True, **kw)
+    bidx, bsc = hk.baseline_select(dv["q"], dv["k"], dv["w"], k, **kw)
+    torch.cuda.synchronize()
+    assert st["n_failed"] == 0, st
+    assert np.array_equal(_np(idx), _np(bidx))
+    assert np.array_equal(_np(sc).view(np.uint32), _np(bsc).view(np.uint32))
+    qs = np.unique(np.concatenate([np.arange(n - 48, n),
+                                   np.random.default_rng(97).choice(n - 48, 48, replace=False)]))
+    ref_idx, ref_val = oracle.select(inp, queries=qs)
+    for j, i in enumerate(qs):
+        assert np.array_equal(_np(idx)[i], ref_idx[j]), f"query {i}"
+        assert np.array_equal(_np(sc)[i], ref_val[j].astype(np.float32)), f"query {i}"

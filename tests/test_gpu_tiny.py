@@ -127,11 +127,11 @@ def test_ragged_shapes_bit_exact(hk, L, n, H, d, k, seed):
     assert np.all(np.isneginf(_np(rep)[~ok]))
 
 
-@pytest.mark.parametrize("fmt,L,n", [("bf16", 12000, 8190), ("mxfp8", 8000, 4094),
+@pytest.mark.parametrize("fmt,L,n", [("bf16", 12000, 8190), ("mxfp8", 12000, 8190),
                                      ("mxfp4", 8000, 4094)])
 def test_one_split_with_partial_last_group(hk, fmt, L, n):
-    """n queries fill 512 query groups (16 per group for bf16, 8 for the scaled
-    formats), so the fused kernel runs one key split per query -- each wave
+    """n queries fill 512 query groups (16 per group, 8 for MXFP4), so the
+    fused kernel runs one key split per query -- each wave
     the only writer of its queries' candidates -- and the last group is
     partial: its last wave has no query.  Integer inputs (exact in every
     format): the selection equals the oracle bit for bit on 96 queries (the
