@@ -48,11 +48,13 @@ struct Fmt {
     }
   }
 
-  // D += A x B where A is E4M3 (the linear row block) and B this format.
+  // D += A x B where A is the linear row block (E2M3 against E2M1 keys, else
+  // E4M3) and B this format.
+  static constexpr int LIN_CODE = FMT == kMXFP4 ? 2 : 0;  // f8f6f4 code of E2M3 / E4M3
   __device__ __forceinline__ static f32x4 mma_lin(const i32x8& a, const Frag& b, const f32x4& c,
                                                   int sa, int sb) {
     static_assert(SCALED, "bf16 has no linear row block");
-    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, 0, CODE, 0, sa, 0, sb);
+    return __builtin_amdgcn_mfma_scale_f32_16x16x128_f8f6f4(a, b, c, LIN_CODE, CODE, 0, sa, 0, sb);
   }
 
   // Bytes of one k-step slice of a row (KMMA elements).

@@ -56,7 +56,7 @@ struct QueryTile {
       uint32_t code[kLinPieces];
       int scale[kLinPieces];
       lin_v<FMT, D, 2>(q, w, q_scale, H, qi, 2 * lane, v);
-      lin_split<2, 64>(v, code, scale);
+      lin_split<FMT, 2, 64>(v, code, scale);
       lin_store<2>(lds, lane, code, scale);
       wave_lds_sync();
       lin_frag<FMT>(lds, r, g, lin, lsa);

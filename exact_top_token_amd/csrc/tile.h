@@ -31,10 +31,13 @@
 // these formats the epilogue costs about as much as the MFMAs, and this takes
 // 4-5% off the scoring time at the 1M shape (bf16 keeps max + fma: there the
 // extra row block costs more than it saves and its registers do not fit).  v is
-// fp32; the MFMA operand carries it as kLinPieces E4M3 rows with one E8M0
-// scale each, piece j being the rounding of what pieces 0..j-1 left over (see
-// lin_split), so that the pieces sum to v within 2^-24 of its largest element
-// and exactly whenever v has fewer significant bits than that.
+// fp32; the MFMA operand carries it as kLinPieces rows of 4-significant-bit
+// elements with one E8M0 scale each, piece j being the rounding of what pieces
+// 0..j-1 left over (see lin_split), so that the pieces sum to v within 2^-24
+// of its largest element and exactly whenever v has fewer significant bits
+// than that.  The elements are E4M3 against E4M3 keys and FP6 E2M3 against
+// MXFP4's E2M1 keys: the MFMA runs at the rate of its wider operand, and an
+// E4M3 row block costs an E2M1 key tile twice what an E2M3 one does.
 #pragma once
 
 #include "common.h"
@@ -62,6 +65,16 @@ __device__ __forceinline__ float e2m1_top(uint32_t t) {
 // E8M0 scale byte (< 255) -> 2^(s - 127).
 __device__ __forceinline__ float e8m0_value(uint32_t s) {
   return s ? __uint_as_float(s << 23) : 0x1p-127f;
+}
+
+// E2M3 code (6 bits: sign, 2 exponent bits with bias 1, 3 mantissa bits) of
+// a value that E2M3 holds exactly (|p| <= 7.5).
+__device__ __forceinline__ uint32_t e2m3_code(float p) {
+  const uint32_t u = __float_as_uint(p), a = u & 0x7FFFFFFFu;
+  const float m = __uint_as_float(a);
+  const uint32_t mag = m >= 1.0f ? ((((a >> 23) - 126u) << 3) | ((a >> 20) & 7u))
+                                 : (uint32_t)(m * 8.0f);
+  return ((u >> 26) & 0x20u) | mag;
 }
 
 // E4M3 byte of a value that E4M3 holds exactly (|p| <= 448).
@@ -116,17 +129,22 @@ __device__ __forceinline__ void lin_v(const uint8_t* __restrict__ q, const float
   }
 }
 
-// Splits v into kLinPieces E4M3 pieces: NE elements per lane, one query per
-// LANES consecutive lanes (32: a half wave, 64: the whole wave).  code[j]
-// packs this lane's codes of piece j (element i in byte i); scale[j] is piece
-// j's E8M0 scale byte, the same in all the query's lanes.  Piece j's scale
-// 2^e puts the largest remaining magnitude m in [128, 256) (e = floor(log2 m)
-// - 7, at least -127); each element is rounded to E4M3 at that scale (ties to
-// even: 4 significant bits, or steps of 2^-9 in the subnormal range) and the
-// exact rounding error is what piece j + 1 splits.
-template <int NE, int LANES>
+// Splits v into kLinPieces pieces of the linear row block's element format
+// (E2M3 for MXFP4, else E4M3): NE elements per lane, one query per LANES
+// consecutive lanes (32: a half wave, 64: the whole wave).  code[j] packs
+// this lane's codes of piece j (element i in byte i); scale[j] is piece j's
+// E8M0 scale byte, the same in all the query's lanes.  Piece j's scale 2^e
+// puts the largest remaining magnitude m in the format's top binades below
+// its largest value ([128, 256) for E4M3, [2, 4) for E2M3; e at least -127);
+// each element is rounded to the format at that scale (ties to even: 4
+// significant bits, or the subnormal step: 2^-9 for E4M3, 2^-3 for E2M3) and
+// the exact rounding error is what piece j + 1 splits.
+template <int FMT, int NE, int LANES>
 __device__ __forceinline__ void lin_split(const float (&v)[NE], uint32_t (&code)[kLinPieces],
                                           int (&scale)[kLinPieces]) {
+  constexpr bool FP6 = FMT == kMXFP4;
+  constexpr int TOP = FP6 ? 1 : 7;      // floor(log2 m) - e
+  constexpr int MIN_EX = FP6 ? 0 : -6;  // smallest normal binade
   float res[NE];
 #pragma unroll
   for (int i = 0; i < NE; ++i) res[i] = v[i];
@@ -137,21 +155,21 @@ __device__ __forceinline__ void lin_split(const float (&v)[NE], uint32_t (&code)
     for (int i = 1; i < NE; ++i) m = __builtin_fmaxf(m, __builtin_fabsf(res[i]));
 #pragma unroll
     for (int off = 1; off < LANES; off <<= 1) m = __builtin_fmaxf(m, __shfl_xor(m, off));
-    const int e = max((int)((__float_as_uint(m) >> 23) & 0xFFu) - 134, -127);  // <= 120
+    const int e = max((int)((__float_as_uint(m) >> 23) & 0xFFu) - 127 - TOP, -127);  // <= 126
     scale[j] = e + 127;
     const float down = __uint_as_float((uint32_t)(127 - e) << 23);               // 2^-e
     const float up = e >= -126 ? __uint_as_float((uint32_t)(127 + e) << 23) : 0x1p-127f;
     uint32_t c = 0;
 #pragma unroll
     for (int i = 0; i < NE; ++i) {
-      const float x = res[i] * down;  // |x| < 256
-      const int ex = max((int)((__float_as_uint(x) >> 23) & 0xFFu) - 127, -6);
+      const float x = res[i] * down;  // |x| < 2^(TOP + 1)
+      const int ex = max((int)((__float_as_uint(x) >> 23) & 0xFFu) - 127, MIN_EX);
       // x + 1.5 * 2^(ex + 20) has unit 2^(ex - 3): adding and removing it
-      // rounds x to E4M3's step at x's binade
+      // rounds x to the format's step at x's binade
       const float magic = __uint_as_float(((uint32_t)(ex + 147) << 23) | 0x400000u);
       const float p = (x + magic) - magic;
       res[i] -= p * up;  // exact
-      c |= e4m3_code(p) << (8 * i);
+      c |= (FP6 ? e2m3_code(p) : e4m3_code(p)) << (8 * i);
     }
     code[j] = c;
   }
@@ -180,19 +198,36 @@ __device__ __forceinline__ void lin_store(uint32_t* reg, int l, const uint32_t (
 }
 
 // The linear row block's A fragment of lane group g holding piece j of the
-// query in `reg` (j >= kLinPieces: a zero row), in the chunk order of the
-// format's k-step (E4M3 elements d 32g .. 32g + 31 for per-token FP8, d 16g ..
-// 16g + 15 and 64 + 16g .. 64 + 16g + 15 for the MX order), and its scale.
+// query in `reg` (j >= kLinPieces: a zero row), in the order the format's
+// k-step takes its elements, and its scale.  E4M3: elements d 32g .. 32g + 31
+// for per-token FP8 (the key fragments' order), d 16g .. 16g + 15 and 64 + 16g
+// .. 64 + 16g + 15 for MXFP8 (the instruction's K order).  E2M3 against E2M1
+// keys: elements d 32g .. 32g + 31, element p in bits 6p .. 6p + 5 of the
+// first six registers (the instruction's FP6 operand layout, measured on
+// gfx950 with single-element operands).
 template <int FMT>
 __device__ __forceinline__ void lin_frag(const uint32_t* reg, int j, int g, i32x8& a, int& sa) {
   a = i32x8{0, 0, 0, 0, 0, 0, 0, 0};
   sa = 127;
   if (j < kLinPieces) {
     const uint32_t* p = reg + 32 * j;
-    const int o0 = FMT == kFP8 ? 8 * g : 4 * g, o1 = FMT == kFP8 ? 8 * g + 4 : 16 + 4 * g;
+    const int o0 = FMT == kMXFP8 ? 4 * g : 8 * g, o1 = FMT == kMXFP8 ? 16 + 4 * g : 8 * g + 4;
     const u32x4 lo = *reinterpret_cast<const u32x4*>(p + o0);
     const u32x4 hi = *reinterpret_cast<const u32x4*>(p + o1);
-    a = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    if constexpr (FMT == kMXFP4) {
+      const uint32_t w[8] = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+      uint32_t b[6] = {0, 0, 0, 0, 0, 0};
+#pragma unroll
+      for (int e = 0; e < 32; ++e) {
+        const uint32_t c = (w[e >> 2] >> (8 * (e & 3))) & 0x3Fu;
+        const int bit = 6 * e;
+        b[bit >> 5] |= c << (bit & 31);
+        if ((bit & 31) > 26) b[(bit >> 5) + 1] |= c >> (32 - (bit & 31));
+      }
+      a = i32x8{(int)b[0], (int)b[1], (int)b[2], (int)b[3], (int)b[4], (int)b[5], 0, 0};
+    } else {
+      a = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3], (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
+    }
     sa = (int)reg[32 * kLinPieces + j];
   }
 }
@@ -237,7 +272,7 @@ struct PairTile {
       uint32_t code[kLinPieces];
       int scale[kLinPieces];
       lin_v<FMT, D, 4>(q, w, q_scale, H, (lane >> 5) ? qb : qa, 4 * (lane & 31), v);
-      lin_split<4, 32>(v, code, scale);
+      lin_split<FMT, 4, 32>(v, code, scale);
       lin_store<4>(lds + (lane >> 5) * kLinWords, lane & 31, code, scale);
       wave_lds_sync();
       const int r = lane & 15;
