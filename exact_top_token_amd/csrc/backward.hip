@@ -391,16 +391,23 @@ __global__ void __launch_bounds__(kRsThreads) rs_scan_kernel(uint32_t* hist, int
 
 // Stable scatter of one tile by its 8-bit digit.  Entries are taken in
 // rounds of 256 (round, wave, lane order = input order); within a wave the
-// entries with the same digit are found with 8 bit-plane ballots.
+// entries with the same digit are found with 8 bit-plane ballots.  The tile
+// is first arranged by digit in LDS and then written out run by run, so
+// consecutive lanes store consecutive addresses of a digit's run instead of
+// every round scattering single elements over up to 256 runs.
 __global__ void __launch_bounds__(kRsThreads) rs_scatter_kernel(const uint32_t* kin,
                                                                 const uint32_t* vin, uint32_t* kout,
                                                                 uint32_t* vout, int N, int shift,
                                                                 int ntiles, const uint32_t* hist,
                                                                 const uint32_t* tot) {
-  __shared__ uint32_t base[256];
+  __shared__ uint32_t base[256];    // output position of this tile's first entry of digit d
+  __shared__ uint32_t lbase[256];   // LDS position of digit d's next entries
+  __shared__ uint32_t lstart[256];  // LDS position of digit d's first entry
   __shared__ uint32_t wc[kRsThreads / kWave][256];
+  __shared__ uint32_t tk[kRsTile], tv[kRsTile];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
   const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  const int t0 = blockIdx.x * kRsTile;
   {
     // entries of smaller digits (exclusive scan of the 256 digit totals)
     const uint32_t x = tot[tid];
@@ -411,12 +418,32 @@ __global__ void __launch_bounds__(kRsThreads) rs_scatter_kernel(const uint32_t* 
     for (int w = 0; w < wave; ++w) off += wc[0][w];
     __syncthreads();
     base[tid] = off + pre + hist[(int64_t)tid * ntiles + blockIdx.x];
+    wc[1][tid] = 0u;
   }
+  __syncthreads();
+  // this tile's digit counts, then their exclusive scan: where each digit's
+  // entries start in the LDS copy
+  for (int it = 0; it < kRsItems; ++it) {
+    const int e = t0 + it * kRsThreads + tid;
+    if (e < N) atomicAdd(&wc[1][(kin[e] >> shift) & 255u], 1u);
+  }
+  __syncthreads();
+  {
+    const uint32_t x = wc[1][tid];
+    const uint32_t pre = (uint32_t)wave_prefix_excl((int)x);
+    if (lane == 63) wc[0][wave] = pre + x;
+    __syncthreads();
+    uint32_t off = 0u;
+    for (int w = 0; w < wave; ++w) off += wc[0][w];
+    lstart[tid] = off + pre;
+    lbase[tid] = off + pre;
+  }
+  __syncthreads();
 #pragma unroll
   for (int w = 0; w < kRsThreads / kWave; ++w) wc[w][tid] = 0u;
   __syncthreads();
   for (int it = 0; it < kRsItems; ++it) {
-    const int e = blockIdx.x * kRsTile + it * kRsThreads + tid;
+    const int e = t0 + it * kRsThreads + tid;
     const bool valid = e < N;
     const uint32_t key = valid ? kin[e] : 0u;
     const uint32_t val = valid ? vin[e] : 0u;
@@ -432,10 +459,10 @@ __global__ void __launch_bounds__(kRsThreads) rs_scatter_kernel(const uint32_t* 
     if (valid && rank == 0) wc[wave][dg] = (uint32_t)__popcll(peers);
     __syncthreads();
     if (valid) {
-      uint32_t off = base[dg] + (uint32_t)rank;
+      uint32_t off = lbase[dg] + (uint32_t)rank;
       for (int w = 0; w < wave; ++w) off += wc[w][dg];
-      kout[off] = key;
-      vout[off] = val;
+      tk[off] = key;
+      tv[off] = val;
     }
     __syncthreads();
     uint32_t s = 0;
@@ -444,8 +471,17 @@ __global__ void __launch_bounds__(kRsThreads) rs_scatter_kernel(const uint32_t* 
       s += wc[w][tid];
       wc[w][tid] = 0u;
     }
-    base[tid] += s;
+    lbase[tid] += s;
     __syncthreads();
+  }
+  // the tile in digit order: entry i goes to its digit's output run
+  const int n = min(kRsTile, N - t0);
+  for (int i = tid; i < n; i += kRsThreads) {
+    const uint32_t key = tk[i];
+    const uint32_t dg = (key >> shift) & 255u;
+    const uint32_t o = base[dg] + ((uint32_t)i - lstart[dg]);
+    kout[o] = key;
+    vout[o] = tv[i];
   }
 }
 
