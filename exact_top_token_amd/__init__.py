@@ -275,19 +275,21 @@ def baseline_select(q, k, w, topk: int, *, q_scale=None, k_scale=None, q_start=N
     return idx, score
 
 
-def backward_workspace_bytes(q, k, w, topk: int, q_start=None) -> int:
+def backward_workspace_bytes(q, k, w, topk: int, q_start=None, fmt=None) -> int:
     lib = load_library()
-    return int(lib.hytopk_backward_workspace(ctypes.byref(_problem(q, k, w, topk, q_start))))
+    return int(lib.hytopk_backward_workspace(ctypes.byref(_problem(q, k, w, topk, q_start,
+                                                                   fmt=fmt))))
 
 
 def backward(q, k, w, idx, d_score, *, q_scale=None, k_scale=None, q_start=None,
-             want=("dq", "dw", "dk"), workspace=None, out=None):
+             want=("dq", "dw", "dk"), workspace=None, out=None, fmt=None):
     """Indexer backward at the replayed entries idx [n][k] with upstream
     gradient d_score [n][k] (fp32).  Returns a dict with the requested fp32
-    gradients: dq [n][H][d], dw [n][H], dk [L][d]."""
+    gradients: dq [n][H][d], dw [n][H], dk [L][d] (for FP8 / MX inputs, with
+    respect to the decoded values)."""
     import torch
     lib = load_library()
-    prob = _problem(q, k, w, idx.shape[1], q_start)
+    prob = _problem(q, k, w, idx.shape[1], q_start, fmt=fmt)
     for t, name in ((idx, "idx"), (d_score, "d_score")):
         if tuple(t.shape) != (prob.n, prob.k) or not t.is_contiguous() or not t.is_cuda:
             raise ValueError(f"{name} must be a contiguous [n][k] tensor on the GPU")
@@ -298,7 +300,7 @@ def backward(q, k, w, idx, d_score, *, q_scale=None, k_scale=None, q_start=None,
     for name in want:
         if name not in res:
             res[name] = torch.empty(shapes[name], dtype=torch.float32, device=q.device)
-    if "dk" in res and workspace is None:
+    if ("dk" in res or prob.dtype != BF16) and workspace is None:
         need = int(lib.hytopk_backward_workspace(ctypes.byref(prob)))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
     _check(lib.hytopk_backward(ctypes.byref(prob), _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale),

@@ -214,7 +214,7 @@ constexpr int64_t kBwdChunkBytes = int64_t(1) << 33;
 
 struct BwdLayout {
   int64_t chunk;
-  size_t u, k0, v0, k1, v1, hist, total;
+  size_t u, k0, v0, k1, v1, hist, qb, kb, total;
 };
 
 BwdLayout bwd_layout(const hytopk_problem* p) {
@@ -230,6 +230,10 @@ BwdLayout bwd_layout(const hytopk_problem* p) {
   l.k1 = off; off = align_up(off + (size_t)N * 4);
   l.v1 = off; off = align_up(off + (size_t)N * 4);
   l.hist = off; off = align_up(off + hk::bwd_sort_hist_count(N) * 4);
+  if (p->dtype != HYTOPK_BF16) {  // q and k as bf16 for the gradient products
+    l.qb = off; off = align_up(off + (size_t)p->n * p->H * p->d * 2);
+    l.kb = off; off = align_up(off + (size_t)p->L * p->d * 2);
+  }
   l.total = off;
   return l;
 }
@@ -507,14 +511,30 @@ int hytopk_backward(const hytopk_problem* p, const void* q, const void* q_scale,
   g_err.clear();
   int rc = check_problem(p);
   if (rc) return rc;
-  if (p->dtype != HYTOPK_BF16) return fail(HYTOPK_EUNSUPPORTED, "backward supports bf16 only");
   if ((rc = check_inputs(p, q, q_scale, k, k_scale, w))) return rc;
   if (!idx || !d_score) return fail(HYTOPK_EINVAL, "idx and d_score must be non-NULL");
   const BwdLayout l = bwd_layout(p);
-  if (dk && (rc = check_ws(workspace, workspace_bytes, l.total))) return rc;
+  const bool scaled = p->dtype != HYTOPK_BF16;
+  if ((dk || scaled) && (rc = check_ws(workspace, workspace_bytes, l.total))) return rc;
   hipStream_t s = static_cast<hipStream_t>(stream);
   const int K = p->k, D = p->d;
   char* ws = static_cast<char*>(workspace);
+  // Scaled formats: q and k as bf16 (decoded MX values, or FP8 codes whose
+  // per-token scales the query kernel applies).
+  const uint16_t* qb = static_cast<const uint16_t*>(q);
+  const uint16_t* kb = static_cast<const uint16_t*>(k);
+  const bool tok = p->dtype == HYTOPK_FP8_E4M3;
+  if (scaled) {
+    Span sp("bwd_query", s);
+    uint16_t* qd = reinterpret_cast<uint16_t*>(ws + l.qb);
+    uint16_t* kd = reinterpret_cast<uint16_t*>(ws + l.kb);
+    HK_HIP(hk::launch_bwd_dequant(q, tok ? nullptr : q_scale, p->n * p->H, D, p->dtype, qd, s),
+           "backward q decode launch");
+    HK_HIP(hk::launch_bwd_dequant(k, tok ? nullptr : k_scale, p->L, D, p->dtype, kd, s),
+           "backward k decode launch");
+    qb = qd;
+    kb = kd;
+  }
   float* u = dk ? reinterpret_cast<float*>(ws + l.u) : nullptr;
   if (dk) {
     Span sp("bwd_dk", s);
@@ -538,9 +558,11 @@ int hytopk_backward(const hytopk_problem* p, const void* q, const void* q_scale,
       HK_HIP(hk::launch_bwd_sort(b, &sorted_keys, &sorted_rows, s), "backward key sort launch");
     }
     hk::BwdArgs a{};
-    a.q = static_cast<const uint16_t*>(q);
-    a.k = static_cast<const uint16_t*>(k);
+    a.q = qb;
+    a.k = kb;
     a.w = w;
+    a.q_scale = tok ? static_cast<const float*>(q_scale) : nullptr;
+    a.k_scale = tok ? static_cast<const float*>(k_scale) : nullptr;
     a.idx = idx;
     a.dsc = d_score;
     a.dq = dq;

@@ -28,10 +28,21 @@
 // LSD radix sort of (key position, row) pairs groups them by key with entries
 // in query-then-slot order; waves sum each key's rows in that order and add
 // the sum to dk.  Chunks run in order, so dk is bitwise reproducible.
+//
+// Scaled formats: the gradients are taken with respect to the decoded values.
+// A first pass writes q and k as bf16 (bwd_dequant_kernel): MX elements times
+// their block's E8M0 scale, exact in bf16; per-token FP8 codes without their
+// scales (also exact).  The per-token scales qs[t], ks[s] then enter as
+// factors, since c = qs ks c8 with c8 the product of the codes (same sign):
+//   dw[t, h]    = qs[t] * sum_j (dI ks[s_j]) max(c8, 0)
+//   dq[t, h, :] = w * sum_j (dI ks[s_j]) [c8 > 0] k8[s_j, :]
+//   u[t, j, :]  = sum_h dI (w qs[t]) [c8 > 0] q8[t, h, :]
+#include <algorithm>
 #include <type_traits>
 
 #include "common.h"
 #include "launch.h"
+#include "tile.h"
 
 namespace hk {
 
@@ -67,7 +78,8 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, con
   return __builtin_amdgcn_mfma_f32_16x16x32_bf16(a, b, c, 0, 0, 0);
 }
 
-template <int D, bool WITH_U>
+// TOK: per-token FP8 scales a.q_scale / a.k_scale applied as factors.
+template <int D, bool WITH_U, bool TOK>
 __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
   constexpr int NCH = D / 8;   // 16-byte chunks per key row
   constexpr int KS = D / 32;   // k-steps of the c products
@@ -88,14 +100,18 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
   const int ntile2 = (ntile + 1) & ~1;
   const int nslot = (ntile2 + kBwdDepth) * kBwdTK;
   int* ids = dyn;                                   // [nslot] key or -1
-  float* dI = reinterpret_cast<float*>(dyn + nslot);  // [nslot]
+  float* dI = reinterpret_cast<float*>(dyn + nslot);  // [nslot] (u's factor)
+  // dw's and dq's factor dI * ks[key] (TOK), else dI itself
+  float* dIk = TOK ? reinterpret_cast<float*>(dyn + 2 * nslot) : dI;
 
   for (int j = tid; j < nslot; j += kBwdThreads) {
     int key = j < K ? a.idx[(int64_t)qi * K + j] : -1;
     if (key < 0 || key >= a.L) key = -1;  // padding, never dereferenced
     ids[j] = key;
     dI[j] = key >= 0 ? a.dsc[(int64_t)qi * K + j] : 0.0f;
+    if constexpr (TOK) dIk[j] = key >= 0 ? dI[j] * a.k_scale[key] : 0.0f;
   }
+  const float qs = TOK ? a.q_scale[qi] : 1.0f;
 
   // Query fragments of this wave's heads: A operand of c, B operand of c^T.
   bf16x8 qa[KS];
@@ -122,11 +138,12 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
       qt[udb][hs] = pack8(v);
     }
   }
-  float wv[4];
+  float wv[4], wu[4];  // dq's head weights; u's (times qs for TOK)
 #pragma unroll
   for (int r = 0; r < 4; ++r) {
     const int h = 16 * wave + 4 * g + r;
     wv[r] = h < H ? a.w[(int64_t)qi * H + h] : 0.0f;
+    wu[r] = TOK ? wv[r] * qs : wv[r];
   }
   f32x4 dqa[NDB];
 #pragma unroll
@@ -204,13 +221,13 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
 #pragma unroll
     for (int blk = 0; blk < 2; ++blk) {
       const int j = 16 * blk + c16;
-      const float di = dI[t * kBwdTK + j];
+      const float di = dI[t * kBwdTK + j], dik = dIk[t * kBwdTK + j];
       uint32_t hi[4], lo[4];
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const float cv = c[blk][r];
-        dwa[r] = __builtin_fmaf(di, __builtin_fmaxf(cv, 0.0f), dwa[r]);
-        split_bf16(cv > 0.0f ? di * wv[r] : 0.0f, hi[r], lo[r]);
+        dwa[r] = __builtin_fmaf(dik, __builtin_fmaxf(cv, 0.0f), dwa[r]);
+        split_bf16(cv > 0.0f ? di * wu[r] : 0.0f, hi[r], lo[r]);
       }
       uint2* dh = reinterpret_cast<uint2*>(&gt[buf][0][j * kGtW + 16 * wave + 4 * g]);
       uint2* dl = reinterpret_cast<uint2*>(&gt[buf][1][j * kGtW + 16 * wave + 4 * g]);
@@ -227,7 +244,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
 #pragma unroll
         for (int r = 0; r < 4; ++r) {
           uint32_t h, l;
-          split_bf16(dI[t * kBwdTK + 16 * blk + 4 * g + r], h, l);
+          split_bf16(dIk[t * kBwdTK + 16 * blk + 4 * g + r], h, l);
           const bool on = ct[blk][r] > 0.0f;
           vh[4 * blk + r] = on ? h : 0u;
           vl[4 * blk + r] = on ? l : 0u;
@@ -301,29 +318,91 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
       v += __shfl_xor(v, 4);
       v += __shfl_xor(v, 8);
       const int h = 16 * wave + 4 * g + r;
+      if constexpr (TOK) v *= qs;
       if (c16 == 0 && h < H) a.dw[(int64_t)qi * H + h] = v;
     }
   }
 }
 
-template <int D, bool WITH_U>
+template <int D, bool WITH_U, bool TOK>
 static hipError_t bwd_query_d(const BwdArgs& a, hipStream_t s) {
   const int ntile = (a.topk + kBwdTK - 1) / kBwdTK;
-  const size_t dyn = (size_t)(((ntile + 1) & ~1) + kBwdDepth) * kBwdTK * 8;
-  hipError_t e = hipFuncSetAttribute((const void*)bwd_query_kernel<D, WITH_U>,
+  const size_t dyn = (size_t)(((ntile + 1) & ~1) + kBwdDepth) * kBwdTK * (TOK ? 12 : 8);
+  hipError_t e = hipFuncSetAttribute((const void*)bwd_query_kernel<D, WITH_U, TOK>,
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
   if (e != hipSuccess) return e;
-  hipLaunchKernelGGL((bwd_query_kernel<D, WITH_U>), dim3((unsigned)a.nq), dim3(kBwdThreads), dyn, s,
-                     a);
+  hipLaunchKernelGGL((bwd_query_kernel<D, WITH_U, TOK>), dim3((unsigned)a.nq), dim3(kBwdThreads),
+                     dyn, s, a);
   return hipGetLastError();
 }
 
 hipError_t launch_bwd_query(const BwdArgs& a, int d, hipStream_t s) {
   if (a.nq <= 0) return hipSuccess;
   const bool u = a.u != nullptr;
-  if (d == 64) return u ? bwd_query_d<64, true>(a, s) : bwd_query_d<64, false>(a, s);
-  if (d == 128) return u ? bwd_query_d<128, true>(a, s) : bwd_query_d<128, false>(a, s);
-  return hipErrorInvalidValue;
+  if (d == 64) return u ? bwd_query_d<64, true, false>(a, s) : bwd_query_d<64, false, false>(a, s);
+  if (d != 128) return hipErrorInvalidValue;
+  if (a.q_scale && a.k_scale)
+    return u ? bwd_query_d<128, true, true>(a, s) : bwd_query_d<128, false, true>(a, s);
+  return u ? bwd_query_d<128, true, false>(a, s) : bwd_query_d<128, false, false>(a, s);
+}
+
+// q or k of a scaled format as bf16 bits, 8 elements per thread and step:
+// MX elements times their block's E8M0 scale, per-token FP8 codes as they
+// are (their scales are applied by the query kernel).  Both are exact in
+// bf16 (an MX product unless it falls below bf16's normal range, where it is
+// rounded to nearest).  x: rows of d elements (E2M1: d / 2 bytes); scale:
+// E8M0 bytes [rows][d / 32] (MX only).
+template <int FMT>
+__global__ void bwd_dequant_kernel(const uint8_t* __restrict__ x, const uint8_t* __restrict__ scale,
+                                   int64_t rows, int d, uint16_t* __restrict__ out) {
+  const int64_t n8 = rows * d / 8;
+  for (int64_t i = blockIdx.x * (int64_t)blockDim.x + threadIdx.x; i < n8;
+       i += (int64_t)gridDim.x * blockDim.x) {
+    const int64_t e0 = 8 * i;  // first element; 8 elements never straddle a row or a block
+    float v[8];
+    if constexpr (FMT == kMXFP4) {
+      const uint32_t w = *reinterpret_cast<const uint32_t*>(x + e0 / 2);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = e2m1_top(w << (28 - 4 * j));
+    } else {
+      const uint2 w = *reinterpret_cast<const uint2*>(x + e0);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] = e4m3_top((j < 4 ? w.x : w.y) << (24 - 8 * (j & 3)));
+    }
+    if constexpr (FMT == kMXFP8 || FMT == kMXFP4) {
+      const int64_t row = e0 / d;
+      const float sc = e8m0_value(scale[row * (d / 32) + (e0 % d) / 32]);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) v[j] *= sc;
+    }
+    uint32_t b[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const uint32_t u = __float_as_uint(v[j]);
+      b[j] = (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;  // nearest, ties to even
+    }
+    *reinterpret_cast<u32x4*>(out + e0) =
+        u32x4{b[0] | (b[1] << 16), b[2] | (b[3] << 16), b[4] | (b[5] << 16), b[6] | (b[7] << 16)};
+  }
+}
+
+hipError_t launch_bwd_dequant(const void* x, const void* scale, int64_t rows, int d, int fmt,
+                              uint16_t* out, hipStream_t s) {
+  const int64_t n8 = rows * d / 8;
+  if (n8 <= 0) return hipSuccess;
+  const int nb = (int)std::min<int64_t>((n8 + 255) / 256, 16384);
+  const auto* xb = static_cast<const uint8_t*>(x);
+  const auto* sb = static_cast<const uint8_t*>(scale);
+  if (fmt == kFP8) {
+    hipLaunchKernelGGL(bwd_dequant_kernel<kFP8>, dim3(nb), dim3(256), 0, s, xb, sb, rows, d, out);
+  } else if (fmt == kMXFP8) {
+    hipLaunchKernelGGL(bwd_dequant_kernel<kMXFP8>, dim3(nb), dim3(256), 0, s, xb, sb, rows, d, out);
+  } else if (fmt == kMXFP4) {
+    hipLaunchKernelGGL(bwd_dequant_kernel<kMXFP4>, dim3(nb), dim3(256), 0, s, xb, sb, rows, d, out);
+  } else {
+    return hipErrorInvalidValue;
+  }
+  return hipGetLastError();
 }
 
 // ----------------------------------------------------------------- dk

@@ -123,6 +123,8 @@ struct BwdArgs {
   float* dq;           // [n][H][d] or null
   float* dw;           // [n][H] or null
   float* u;            // [nq * bwd_padded_k(topk)][d] dk rows of the chunk's entries, or null
+  const float* q_scale;  // [n] per-token FP8 scales of q and k (q, k then hold the codes
+  const float* k_scale;  // [L] as bf16), or null for bf16 / dequantized MX inputs
   int L;
   int H;
   int topk;
@@ -131,6 +133,9 @@ struct BwdArgs {
 };
 
 hipError_t launch_bwd_query(const BwdArgs& a, int d, hipStream_t s);
+// Scaled-format q or k ([rows][d] elements) as bf16 bits for the backward.
+hipError_t launch_bwd_dequant(const void* x, const void* scale, int64_t rows, int d, int fmt,
+                              uint16_t* out, hipStream_t s);
 
 struct DkArgs {
   const int* idx;      // the chunk's [nq][topk] indices (entry e = row-major position)

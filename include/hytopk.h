@@ -180,7 +180,8 @@ int hytopk_baseline_select(const hytopk_problem* p, const void* q, const void* q
                            void* workspace, size_t workspace_bytes, void* stream);
 
 /* Workspace bytes of hytopk_backward (0 on invalid input): the dk rows of one
- * chunk of queries plus the buffers that group them by key.  The chunk size
+ * chunk of queries plus the buffers that group them by key (and, for FP8 and
+ * MX inputs, q and k as bf16: (n * H + L) * d * 2 bytes).  The chunk size
  * depends only on the problem (up to 8 GiB of rows, d * 4 bytes per entry
  * with k padded to an even number of 32-key tiles), so results do not depend
  * on the workspace a caller passes. */
@@ -199,9 +200,13 @@ size_t hytopk_backward_workspace(const hytopk_problem* p);
  * dq, dw, dk may be NULL to skip it (dk NULL skips the workspace traffic).
  * Indices outside [0, L) are padding and contribute nothing.  dk is summed in
  * a fixed order (query ascending, then slot), so results are bitwise
- * reproducible.  bf16 inputs only (HYTOPK_EUNSUPPORTED for fp8).  Products
- * use bf16 MFMA with every fp32 factor split into two bf16 parts (16
- * significant bits) and fp32 accumulation. */
+ * reproducible.  Products use bf16 MFMA with every fp32 factor split into two
+ * bf16 parts (16 significant bits) and fp32 accumulation.  FP8 and MX inputs
+ * are differentiated with respect to their decoded values (code times scale;
+ * dq and dk are gradients of those values): MX q and k are decoded to bf16
+ * (exact), FP8 codes are taken as bf16 with the per-token scales applied as
+ * factors; for these formats the workspace is required whether or not dk is
+ * asked for. */
 int hytopk_backward(const hytopk_problem* p, const void* q, const void* q_scale,
                     const void* k, const void* k_scale, const float* w, const int32_t* idx,
                     const float* d_score, float* dq, float* dw, float* dk,

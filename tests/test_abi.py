@@ -103,9 +103,14 @@ def test_backward_workspace_and_argument_errors(lib):
     assert (8 << 30) <= ws < (8 << 30) + (320 << 20) and ws % 256 == 0
     fake = ctypes.c_void_p(0x1000)
     args = [fake, None, fake, None, fake, fake, fake, fake, fake, fake, fake, 1 << 40, None]
-    # fp8 -> unsupported; NULL idx / d_score -> invalid; small workspace with dk -> -3
+    # fp8 without its scales -> invalid; fp8 needs the workspace (its bf16
+    # copies of q and k) even without dk -> -3; both before any launch.
+    # NULL idx / d_score -> invalid; small workspace with dk -> -3
     p8 = _prob(dtype=hk.FP8_E4M3)
-    assert lib.hytopk_backward(ctypes.byref(p8), *args) == -2
+    assert lib.hytopk_backward(ctypes.byref(p8), *args) == -1
+    a = list(args); a[1] = fake; a[3] = fake; a[9] = None; a[10] = None; a[11] = 0
+    assert lib.hytopk_backward(ctypes.byref(p8), *a) == -3
+    assert lib.hytopk_backward_workspace(ctypes.byref(p8)) == ws + (8192 * 64 + (1 << 20)) * 128 * 2
     a = list(args); a[5] = None
     assert lib.hytopk_backward(ctypes.byref(p), *a) == -1
     a = list(args); a[11] = 16

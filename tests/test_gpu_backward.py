@@ -44,10 +44,17 @@ def _grad(shape, seed, integer):
     return rng.standard_normal(shape).astype(np.float32)
 
 
-def _run(hk, dev, idx, g, want=("dq", "dw", "dk")):
+def _fmt_kw(inp, dev):
+    """Scales and format of a scaled-format problem (empty for bf16)."""
+    if inp.dtype == "bf16":
+        return {}
+    return dict(q_scale=dev["q_scale"], k_scale=dev["k_scale"], fmt=inp.dtype)
+
+
+def _run(hk, dev, idx, g, want=("dq", "dw", "dk"), kw=None):
     idx_t = torch.from_numpy(np.ascontiguousarray(idx, dtype=np.int32)).cuda()
     g_t = torch.from_numpy(np.ascontiguousarray(g, dtype=np.float32)).cuda()
-    res = hk.backward(dev["q"], dev["k"], dev["w"], idx_t, g_t, want=want)
+    res = hk.backward(dev["q"], dev["k"], dev["w"], idx_t, g_t, want=want, **(kw or {}))
     torch.cuda.synchronize()
     return {k: v.cpu().numpy() for k, v in res.items()}
 
@@ -70,7 +77,8 @@ def _assert_close(name, got, ref, scale, amb):
 
 def _integer_case(hk, inp, seed, corrupt=False):
     dev = to_device(inp)
-    idx_t, _ = hk.select(dev["q"], dev["k"], dev["w"], inp.k)
+    kw = _fmt_kw(inp, dev)
+    idx_t, _ = hk.select(dev["q"], dev["k"], dev["w"], inp.k, **kw)
     idx = idx_t.cpu().numpy()
     if corrupt:  # out-of-range indices are padding
         rng = np.random.default_rng(seed)
@@ -78,7 +86,7 @@ def _integer_case(hk, inp, seed, corrupt=False):
         idx[rows, 0] = inp.L + 3
         idx[rows, -1] = -7
     g = _grad(idx.shape, seed, True)
-    got = _run(hk, dev, idx, g)
+    got = _run(hk, dev, idx, g, kw=kw)
     ref = oracle.backward(inp, idx, g)
     for name in ("dq", "dw", "dk"):
         _assert_equal(name, got[name], ref[name])
@@ -123,10 +131,11 @@ def test_backward_reproducible_and_partial_outputs(hk):
 
 def _float_check(hk, inp, seed, nsub):
     dev = to_device(inp)
-    idx_t, sc_t = hk.select(dev["q"], dev["k"], dev["w"], inp.k)
+    kw = _fmt_kw(inp, dev)
+    idx_t, sc_t = hk.select(dev["q"], dev["k"], dev["w"], inp.k, **kw)
     idx, score = idx_t.cpu().numpy(), sc_t.cpu().numpy()
     g = _grad(idx.shape, seed, False)
-    got = _run(hk, dev, idx, g)
+    got = _run(hk, dev, idx, g, kw=kw)
     # dq, dw on a query subset (first and last query included)
     qs = datagen.subset_queries(inp.n, nsub, seed=7)
     ref = oracle.backward(inp, idx[qs], g[qs], qs, amb=AMB)
@@ -167,5 +176,39 @@ def test_mid_backward_float(hk):
 
 
 def test_glm1m_backward_float(hk):
-    say("backward glm1m: L=1048576 n=8192 H=64 d=128 k=2048 (four chunks)")
+    say("backward glm1m: L=1048576 n=8192 H=64 d=128 k=2048 (one 8 GiB chunk)")
     _float_check(hk, datagen.make("glm1m"), 52, 32)
+
+
+# ----------------------------------------------------------- scaled formats
+
+@pytest.mark.parametrize("fmt,H,seed", [("mxfp8", 64, 61), ("mxfp4", 64, 62), ("mxfp4", 8, 63)])
+def test_mx_backward_equals_bf16_on_the_same_values(hk, fmt, H, seed):
+    """MX integer problems decode to the same values as the bf16 problem of the
+    same seed; their backward (with respect to the decoded values) must match
+    the oracle and the bf16 backward bit for bit."""
+    say(f"backward {fmt}: integer problem L=3000 n=200 H={H} d=128 k=256")
+    inp = datagen.make_custom("bwmx", 3000, 200, H, 128, 256, dtype=fmt, dist="int", seed=seed)
+    _, idx, g, got = _integer_case(hk, inp, seed, corrupt=True)
+    bf = datagen.make_custom("bwbf", 3000, 200, H, 128, 256, dtype="bf16", dist="int", seed=seed)
+    ref = _run(hk, to_device(bf), idx, g)
+    for name in ("dq", "dw", "dk"):
+        assert np.array_equal(got[name], ref[name]), name
+
+
+@pytest.mark.parametrize("H,seed", [(8, 64), (64, 65)])
+def test_fp8_backward_exact(hk, H, seed):
+    """Per-token FP8 with integer codes and power-of-two scales: the scales
+    enter as factors (dI k_scale for dq and dw, w q_scale for dk, q_scale on
+    dw); every value stays exact, so the gradients equal the oracle's bit for
+    bit."""
+    from test_gpu_fp8 import _fp8_exact
+    say(f"backward fp8: exact problem L=3000 n=200 H={H} d=128 k=256")
+    _integer_case(hk, _fp8_exact(3000, 200, H, 256, seed), seed, corrupt=True)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp8", "mxfp4"])
+def test_scaled_backward_float(hk, fmt):
+    say(f"backward {fmt}: Gaussian problem L=20000 n=256 H=64 d=128 k=512")
+    inp = datagen.make_custom("bwsc", 20000, 256, 64, 128, 512, dtype=fmt, dist="normal", seed=66)
+    _float_check(hk, inp, 67, 32)
