@@ -68,12 +68,14 @@ def replay_bytes(n, H, d, k, fmt) -> int:
     return n * k * per_entry + n * per_query
 
 
-def backward_bytes(L, n, H, d, k) -> int:
-    """Algorithmic HBM bytes of the bf16 backward: per entry the key row, its
-    index and upstream gradient; per query q and w read, dq and dw written;
-    dk written once."""
-    per_entry = d * 2 + 4 + 4
-    per_query = H * (d * 2 + 4) + H * (d * 4 + 4)
+def backward_bytes(L, n, H, d, k, fmt="bf16") -> int:
+    """Algorithmic HBM bytes of the backward: per entry the key row in its
+    storage format (+ its per-token scale), its index and upstream gradient;
+    per query its rows and weights read, dq and dw written; dk written once."""
+    row = {"bf16": 2 * d, "fp8": d, "mxfp8": d + d // 32, "mxfp4": d // 2 + d // 32}[fmt]
+    tok = 4 if fmt == "fp8" else 0
+    per_entry = row + tok + 4 + 4
+    per_query = H * (row + 4) + tok + H * (d * 4 + 4)
     return n * k * per_entry + n * per_query + L * d * 4
 
 
@@ -252,9 +254,11 @@ def main() -> int:
             log("WARNING: baseline result differs from hytopk_select")
 
     bwd = None
-    if not args.no_backward and not fp8:
+    if not args.no_backward:
         log("backward at the replayed entries (dq, dw, dk)")
-        bws = torch.empty(hk.backward_workspace_bytes(q, k, w, inp.k), dtype=torch.uint8, device=dev)
+        bk = dict(fmt=fmt, q_scale=qs, k_scale=ks) if fp8 else {}
+        bws = torch.empty(hk.backward_workspace_bytes(q, k, w, inp.k, **fk), dtype=torch.uint8,
+                          device=dev)
         gen = torch.Generator(device=dev)
         gen.manual_seed(1234)
         dsc = torch.randn((inp.n, inp.k), generator=gen, dtype=torch.float32, device=dev)
@@ -262,20 +266,20 @@ def main() -> int:
                 "dw": torch.empty((inp.n, inp.H), dtype=torch.float32, device=dev),
                 "dk": torch.empty((inp.L, inp.d), dtype=torch.float32, device=dev)}
         for _ in range(max(1, args.warmup)):
-            hk.backward(q, k, w, idx, dsc, workspace=bws, out=outs)
+            hk.backward(q, k, w, idx, dsc, workspace=bws, out=outs, **bk)
         torch.cuda.synchronize()
         hk.trace_enable(True)
         bev = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True))
                for _ in range(args.steps)]
         for a, b in bev:
             a.record()
-            hk.backward(q, k, w, idx, dsc, workspace=bws, out=outs)
+            hk.backward(q, k, w, idx, dsc, workspace=bws, out=outs, **bk)
             b.record()
         torch.cuda.synchronize()
         bph = hk.trace_read()
         hk.trace_enable(False)
         bms = float(np.median([a.elapsed_time(b) for a, b in bev]))
-        abytes = backward_bytes(inp.L, inp.n, inp.H, inp.d, inp.k)
+        abytes = backward_bytes(inp.L, inp.n, inp.H, inp.d, inp.k, fmt)
         bwd = {"ms": round(bms, 4), "algorithmic_bytes": abytes,
                "gbs": round(abytes / (bms * 1e-3) / 1e9, 1),
                "hbm_frac": round(abytes / (bms * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),

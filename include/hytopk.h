@@ -54,7 +54,7 @@
  *     the calling thread's most recent failure.
  *   * Supported in this version: 1 <= H <= 64 (heads beyond a multiple of 8
  *     are zero-padded; H <= 8 uses a narrow tile); d in {64, 128} for bf16,
- *     d = 128 for FP8 E4M3 and the MX formats; the backward is bf16 only;
+ *     d = 128 for FP8 E4M3 and the MX formats (the backward included);
  *     1 <= k <= 2048; L < 2^31; cap <= 16384 and
  *     m_max <= 16384.  Other shapes return HYTOPK_EUNSUPPORTED.
  */
