@@ -196,15 +196,15 @@ def test_mx_backward_equals_bf16_on_the_same_values(hk, fmt, H, seed):
         assert np.array_equal(got[name], ref[name]), name
 
 
-@pytest.mark.parametrize("H,seed", [(8, 64), (64, 65)])
-def test_fp8_backward_exact(hk, H, seed):
+@pytest.mark.parametrize("H,k,seed", [(8, 256, 64), (64, 256, 65), (20, 100, 68)])
+def test_fp8_backward_exact(hk, H, k, seed):
     """Per-token FP8 with integer codes and power-of-two scales: the scales
     enter as factors (dI k_scale for dq and dw, w q_scale for dk, q_scale on
     dw); every value stays exact, so the gradients equal the oracle's bit for
     bit."""
     from test_gpu_fp8 import _fp8_exact
-    say(f"backward fp8: exact problem L=3000 n=200 H={H} d=128 k=256")
-    _integer_case(hk, _fp8_exact(3000, 200, H, 256, seed), seed, corrupt=True)
+    say(f"backward fp8: exact problem L=3000 n=200 H={H} d=128 k={k}")
+    _integer_case(hk, _fp8_exact(3000, 200, H, k, seed), seed, corrupt=True)
 
 
 @pytest.mark.parametrize("fmt", ["fp8", "mxfp8", "mxfp4"])
