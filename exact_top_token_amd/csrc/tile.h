@@ -29,8 +29,9 @@
 // more MFMA row block computes; the per-head work left for the vector ALUs is
 // one fma with |acc| (an input modifier) instead of a max and an fma.  On
 // these formats the epilogue costs about as much as the MFMAs, and this takes
-// 4-5% off the scoring time at the 1M shape (bf16 keeps max + fma: there the
-// extra row block costs more than it saves and its registers do not fit).  v is
+// 4-5% off the scoring time at the 1M shape for FP8 and MXFP8, about 9% for
+// MXFP4 (bf16 keeps max + fma: there the extra row block costs more than it
+// saves and its registers do not fit).  v is
 // fp32; the MFMA operand carries it as kLinPieces rows of 4-significant-bit
 // elements with one E8M0 scale each, piece j being the rounding of what pieces
 // 0..j-1 left over (see lin_split), so that the pieces sum to v within 2^-24
@@ -46,7 +47,7 @@ namespace hk {
 
 // ------------------------------------------------------------ linear term
 
-constexpr int kLinPieces = 6;   // E4M3 pieces of v (about 4 bits each)
+constexpr int kLinPieces = 6;   // pieces of v (E4M3 or E2M3, about 4 bits each)
 constexpr int kLinWords = 200;  // LDS dwords per query: 32 per piece, the scales, padding
 
 // Element decoders.  fp32 denormals are kept (the kernels' float mode), so
