@@ -29,7 +29,10 @@ if ROOT not in sys.path:
 PEAK_TFLOPS = {"bf16": 2516.6, "fp8": 5033.2, "mxfp8": 5033.2, "mxfp4": 10066.3}  # MI355X dense MFMA
 PEAK_HBM_GBS = 8000.0
 METRIC = "HyTopK select ms + TFLOP/s (%MFMA peak) at L=1M,n=8192,k=2048; replay ms"
-TRAFFIC_FILE = os.path.join(ROOT, "profiles", "traffic_score_tile_glm1m_bf16.txt")
+def traffic_file(workload: str) -> str:
+    """Stored HBM counters of the score kernel for a workload (profiles/)."""
+    name = "glm1m_bf16" if workload == "glm1m" else workload
+    return os.path.join(ROOT, "profiles", f"traffic_score_tile_{name}.txt")
 KERNEL_SOURCES = ["exact_top_token_amd/csrc/score.hip", "exact_top_token_amd/csrc/tile.h",
                   "exact_top_token_amd/csrc/common.h"]
 
@@ -224,9 +227,9 @@ def main() -> int:
     achieved = sel_flops / (score_ms * 1e-3) / 1e12 if score_ms > 0 else None
 
     traffic = None
-    if os.path.exists(TRAFFIC_FILE):
+    if os.path.exists(traffic_file(args.workload)):
         try:
-            tr = json.load(open(TRAFFIC_FILE))
+            tr = json.load(open(traffic_file(args.workload)))
             if tr.get("kernel_hash") == kernel_hash() and tr.get("workload") == args.workload:
                 traffic = tr.get("bytes_per_launch")
         except Exception:
