@@ -212,3 +212,21 @@ def test_scaled_backward_float(hk, fmt):
     say(f"backward {fmt}: Gaussian problem L=20000 n=256 H=64 d=128 k=512")
     inp = datagen.make_custom("bwsc", 20000, 256, 64, 128, 512, dtype=fmt, dist="normal", seed=66)
     _float_check(hk, inp, 67, 32)
+
+
+@pytest.mark.parametrize("fmt", ["fp8", "mxfp4"])
+def test_scaled_backward_partial_outputs(hk, fmt):
+    """dq / dw without dk (the scaled formats still need the workspace for
+    their bf16 copies of q and k) and dk alone give the bits of the full call."""
+    say(f"backward {fmt}: partial outputs")
+    inp = datagen.make_custom("bwpart", 4000, 96, 64, 128, 256, dtype=fmt, dist="normal", seed=69)
+    dev = to_device(inp)
+    kw = _fmt_kw(inp, dev)
+    idx_t, _ = hk.select(dev["q"], dev["k"], dev["w"], inp.k, **kw)
+    idx = idx_t.cpu().numpy()
+    g = _grad(idx.shape, 69, False)
+    full = _run(hk, dev, idx, g, kw=kw)
+    part = _run(hk, dev, idx, g, want=("dq", "dw"), kw=kw)
+    only_k = _run(hk, dev, idx, g, want=("dk",), kw=kw)
+    assert np.array_equal(full["dq"], part["dq"]) and np.array_equal(full["dw"], part["dw"])
+    assert np.array_equal(full["dk"], only_k["dk"])
