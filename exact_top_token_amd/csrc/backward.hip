@@ -80,15 +80,20 @@ __device__ __forceinline__ f32x4 mfma_bf16(const bf16x8& a, const bf16x8& b, con
 
 // TOK: per-token FP8 scales a.q_scale / a.k_scale applied as factors.
 template <int D, bool WITH_U, bool TOK>
-__global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
+__global__ void __launch_bounds__(kBwdThreads) __attribute__((amdgpu_waves_per_eu(3)))
+bwd_query_kernel(BwdArgs a) {
   constexpr int NCH = D / 8;   // 16-byte chunks per key row
   constexpr int KS = D / 32;   // k-steps of the c products
   constexpr int NDB = D / 16;  // dim blocks of dq
   constexpr int UDB = D / 64;  // dim blocks of u per wave (a wave owns D / 4 dims)
 
-  __shared__ __attribute__((aligned(16))) uint16_t krow[2][kBwdTK * D];
+  // krow and gt are single buffers: every read of krow (the c products) and
+  // of gt (the u products) of tile t comes before a barrier that all waves
+  // pass before tile t + 1 writes them.  kt is read after tile t's second
+  // barrier, so it alternates.  (LDS of three workgroups fits one CU.)
+  __shared__ __attribute__((aligned(16))) uint16_t krow[kBwdTK * D];
   __shared__ __attribute__((aligned(16))) uint16_t kt[2][D * kKtW];
-  __shared__ __attribute__((aligned(16))) uint16_t gt[2][2][kBwdTK * kGtW];
+  __shared__ __attribute__((aligned(16))) uint16_t gt[2][kBwdTK * kGtW];
   extern __shared__ int dyn[];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4, c16 = lane & 15;
@@ -179,7 +184,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
       const int j = 4 * kg + v;
       x[v] = pf[slot][v];
       if (ids[tile * kBwdTK + j] < 0) x[v] = uint2{0u, 0u};
-      *reinterpret_cast<uint2*>(&krow[buf][j * D + (((q4 >> 1) ^ (j & (NCH - 1))) * 8) + 4 * (q4 & 1)]) = x[v];
+      *reinterpret_cast<uint2*>(&krow[j * D + (((q4 >> 1) ^ (j & (NCH - 1))) * 8) + 4 * (q4 & 1)]) = x[v];
     }
 #pragma unroll
     for (int e = 0; e < 4; ++e) {
@@ -212,7 +217,7 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
 #pragma unroll
       for (int ks = 0; ks < KS; ++ks) {
         const bf16x8 kb = *reinterpret_cast<const bf16x8*>(
-            &krow[buf][j * D + (((4 * ks + g) ^ (j & (NCH - 1))) * 8)]);
+            &krow[j * D + (((4 * ks + g) ^ (j & (NCH - 1))) * 8)]);
         c[blk] = mfma_bf16(qa[ks], kb, c[blk]);   // lane: heads 4g + r, key j
         ct[blk] = mfma_bf16(kb, qa[ks], ct[blk]);  // lane: keys 16 blk + 4g + r, head c16
       }
@@ -229,8 +234,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
         dwa[r] = __builtin_fmaf(dik, __builtin_fmaxf(cv, 0.0f), dwa[r]);
         split_bf16(cv > 0.0f ? di * wu[r] : 0.0f, hi[r], lo[r]);
       }
-      uint2* dh = reinterpret_cast<uint2*>(&gt[buf][0][j * kGtW + 16 * wave + 4 * g]);
-      uint2* dl = reinterpret_cast<uint2*>(&gt[buf][1][j * kGtW + 16 * wave + 4 * g]);
+      uint2* dh = reinterpret_cast<uint2*>(&gt[0][j * kGtW + 16 * wave + 4 * g]);
+      uint2* dl = reinterpret_cast<uint2*>(&gt[1][j * kGtW + 16 * wave + 4 * g]);
       *dh = uint2{hi[0] | (hi[1] << 16), hi[2] | (hi[3] << 16)};
       *dl = uint2{lo[0] | (lo[1] << 16), lo[2] | (lo[3] << 16)};
     }
@@ -274,8 +279,8 @@ __global__ void __launch_bounds__(kBwdThreads) bwd_query_kernel(BwdArgs a) {
         bf16x8 gh[2], gl[2];
 #pragma unroll
         for (int hs = 0; hs < 2; ++hs) {
-          gh[hs] = *reinterpret_cast<const bf16x8*>(&gt[buf][0][j * kGtW + 8 * g + 32 * hs]);
-          gl[hs] = *reinterpret_cast<const bf16x8*>(&gt[buf][1][j * kGtW + 8 * g + 32 * hs]);
+          gh[hs] = *reinterpret_cast<const bf16x8*>(&gt[0][j * kGtW + 8 * g + 32 * hs]);
+          gl[hs] = *reinterpret_cast<const bf16x8*>(&gt[1][j * kGtW + 8 * g + 32 * hs]);
         }
         const int jg = t * kBwdTK + j;
 #pragma unroll
