@@ -66,6 +66,35 @@ def test_threshold_rank_clamps():
     assert oracle.threshold_rank(1040385, 2048, 8192) == 49
 
 
+THRESHOLD_CASES = os.path.join(os.path.dirname(__file__), "golden", "threshold_cases.json")
+
+
+def _threshold_case_row(case) -> np.ndarray:
+    if "row" in case:
+        return np.array(case["row"], dtype=np.float64)
+    ctx = case["ctx"]
+    if case["row_rule"].startswith("ctx = 8192"):
+        row = np.full(ctx, -1.0)
+        row[0::2] = np.arange(ctx // 2) // 4
+        return row
+    return np.arange(ctx, dtype=np.float64)
+
+
+@pytest.mark.parametrize("case", json.load(open(THRESHOLD_CASES))["cases"],
+                         ids=lambda c: c["name"])
+def test_threshold_hand_computed(case):
+    """tau, rank, sample count and candidate count against values derived by
+    hand from the sampling rule (duplicates counted separately; M from L)."""
+    row = _threshold_case_row(case)
+    tau, r, mq = oracle.threshold(row, case["k"], case["L"])
+    assert (mq, r, tau) == (case["M_q"], case["r"], case["tau"])
+    assert oracle.candidates(row, tau).size == case["count"]
+    p = oracle.predict_row(row, case["k"], case["L"], cap=10 ** 6)
+    assert (p["tau"], p["cnt"]) == (case["tau"], case["count"])
+    for wrong_tau, wrong_count in case["wrong"].values():
+        assert (tau, case["count"]) != (wrong_tau, wrong_count)
+
+
 # ---------------------------------------------------------------- codecs
 
 def test_bf16_decode_special_values():
