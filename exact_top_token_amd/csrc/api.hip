@@ -113,6 +113,8 @@ int check_problem(const hytopk_problem* p) {
   if (p->L <= 0 || p->n <= 0 || p->q_start < 0) return fail(HYTOPK_EINVAL, "L, n must be > 0 and q_start >= 0");
   if (!p->q_pos && p->q_start + p->n > p->L) return fail(HYTOPK_EINVAL, "q_start + n > L");
   if (p->L >= (int64_t(1) << 31)) return fail(HYTOPK_EUNSUPPORTED, "L >= 2^31");
+  if (p->n >= (int64_t(1) << 31)) return fail(HYTOPK_EUNSUPPORTED, "n >= 2^31");
+  if (p->q_start >= (int64_t(1) << 31)) return fail(HYTOPK_EUNSUPPORTED, "q_start >= 2^31");
   if (p->k <= 0) return fail(HYTOPK_EINVAL, "k must be > 0");
   if (p->k > kMaxK) return fail(HYTOPK_EUNSUPPORTED, "k > 2048");
   if (p->H <= 0 || p->d <= 0) return fail(HYTOPK_EINVAL, "H, d must be > 0");
@@ -137,9 +139,9 @@ Params resolve(const hytopk_problem* p, const hytopk_params* prm) {
   r.cap = (prm && prm->cap) ? prm->cap : 6 * p->k;
   r.max_recover = (prm && prm->max_recover) ? prm->max_recover : 64;
   r.force_path = prm ? prm->force_path : HYTOPK_PATH_AUTO;
-  int64_t dflt = std::max<int64_t>(r.max_recover, (int64_t(1) << 29) / p->L);
-  dflt = std::min<int64_t>(dflt, p->n);
-  r.rows_chunk = (prm && prm->rows_chunk) ? prm->rows_chunk : (int)std::max<int64_t>(1, dflt);
+  // rows buffer: max_recover rows by default (one recovery pass)
+  const int64_t dflt = std::min<int64_t>(p->n, std::max(1, r.max_recover));
+  r.rows_chunk = (prm && prm->rows_chunk) ? prm->rows_chunk : (int)dflt;
   return r;
 }
 
@@ -162,9 +164,16 @@ int sample_count(const hytopk_problem* p, const Params& r) {
 }
 
 struct Layout {
-  size_t tau, cnt, failed, stats, cand, rows, total;
+  size_t tau, cnt, failed, stats, cand, rows, split, total;
   int rows_n;
 };
+
+// Scratch of the split row top-k for up to `rows` rows (0 when that many rows
+// fill the GPU one workgroup per row).
+size_t split_bytes(const hytopk_problem* p, int rows) {
+  if (rows > hk::kRowSplitMaxRows) return 0;
+  return hk::row_select_scratch_bytes(rows, hk::row_select_max_chunks(p->L), p->k);
+}
 
 Layout layout(const hytopk_problem* p, const Params& r) {
   Layout l{};
@@ -175,8 +184,9 @@ Layout layout(const hytopk_problem* p, const Params& r) {
   l.failed = off; off = align_up(off + n * 4);
   l.stats = off; off = align_up(off + sizeof(hk::DevStats));
   l.cand = off; off = align_up(off + n * (size_t)r.cap * 8);
-  l.rows_n = std::max(r.max_recover, std::min(r.rows_chunk, (int)p->n));
+  l.rows_n = (int)std::min<int64_t>(r.rows_chunk, p->n);
   l.rows = off; off = align_up(off + (size_t)l.rows_n * (size_t)p->L * 4);
+  l.split = off; off = align_up(off + split_bytes(p, l.rows_n));
   l.total = off;
   return l;
 }
@@ -259,10 +269,12 @@ int64_t ctx_bound(const hytopk_problem* p, int64_t last) {
   return p->q_pos ? p->L : p->q_start + last;
 }
 
-// Score `nq` queries (qlist or q_offset..) into rows, then row top-k.
+// Score `nq` queries (qlist or q_offset..) into rows, then row top-k: split
+// over many workgroups per row when the rows are few and `split` scratch is
+// given, else one workgroup per row.
 int rows_path(const hytopk_problem* p, const hk::ScoreArgs& base, const int* qlist, int q_offset,
               int nq, int64_t maxctx, float* rows, int32_t* out_idx, float* out_score,
-              hipStream_t s) {
+              void* split, hipStream_t s) {
   hk::ScoreArgs a = base;
   a.rows = rows;
   a.row_stride = p->L;
@@ -274,8 +286,25 @@ int rows_path(const hytopk_problem* p, const hk::ScoreArgs& base, const int* qli
     Span sp("score_rows", s);
     HK_HIP(hk::launch_score(a, p->d, p->dtype, s), "score rows launch");
   }
-  {
-    Span sp("row_topk", s);
+  Span sp("row_topk", s);
+  if (split && nq <= hk::kRowSplitMaxRows) {
+    hk::RowSelArgs r{};
+    r.rows = rows;
+    r.row_stride = p->L;
+    r.qlist = qlist;
+    r.q_offset = q_offset;
+    r.nq = nq;
+    r.qpos = p->q_pos;
+    r.qfirst = p->q_first;
+    r.q_start = (int)p->q_start;
+    r.topk = p->k;
+    r.L = (int)p->L;
+    hk::row_select_chunks(nq, maxctx, p->L, r.nchunk, r.chunk_len);
+    r.scratch = split;
+    r.out_idx = out_idx;
+    r.out_score = out_score;
+    HK_HIP(hk::launch_row_select_split(r, s), "split row top-k launch");
+  } else {
     HK_HIP(hk::launch_row_topk(rows, p->L, qlist, q_offset, nq, p->q_pos, p->q_first,
                                (int)p->q_start, p->k, (int)p->L, out_idx, out_score, s),
            "row top-k launch");
@@ -372,6 +401,7 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
   hk::DevStats* dst = reinterpret_cast<hk::DevStats*>(ws + l.stats);
   uint2* cand = reinterpret_cast<uint2*>(ws + l.cand);
   float* rows = reinterpret_cast<float*>(ws + l.rows);
+  void* split = split_bytes(p, l.rows_n) ? static_cast<void*>(ws + l.split) : nullptr;
   const int fmt = p->dtype;
   const int n = (int)p->n;
   const int64_t maxctx = ctx_bound(p, p->n);
@@ -425,14 +455,15 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
     // Recovery: full score rows for the flagged queries only, then row top-k.
     for (int f0 = 0; f0 < hs.n_failed; f0 += l.rows_n) {
       const int nf = std::min(l.rows_n, hs.n_failed - f0);
-      rc = rows_path(p, base, failed + f0, 0, nf, maxctx, rows, out_idx, out_score, s);
+      rc = rows_path(p, base, failed + f0, 0, nf, maxctx, rows, out_idx, out_score, split, s);
       if (rc) return rc;
     }
   } else {
     // Full rescore: every query through the row path, in chunks of rows_n.
     for (int c0 = 0; c0 < n; c0 += l.rows_n) {
       const int nc = std::min(l.rows_n, n - c0);
-      rc = rows_path(p, base, nullptr, c0, nc, ctx_bound(p, c0 + nc), rows, out_idx, out_score, s);
+      rc = rows_path(p, base, nullptr, c0, nc, ctx_bound(p, c0 + nc), rows, out_idx, out_score,
+                     split, s);
       if (rc) return rc;
     }
   }
@@ -494,7 +525,7 @@ int hytopk_baseline_select(const hytopk_problem* p, const void* q, const void* q
   if ((rc = check_ws(workspace, workspace_bytes, hytopk_baseline_workspace(p)))) return rc;
   const hk::ScoreArgs base = score_args(p, q, q_scale, k, k_scale, w);
   return rows_path(p, base, nullptr, 0, (int)p->n, ctx_bound(p, p->n),
-                   static_cast<float*>(workspace), out_idx, out_score,
+                   static_cast<float*>(workspace), out_idx, out_score, nullptr,
                    static_cast<hipStream_t>(stream));
 }
 

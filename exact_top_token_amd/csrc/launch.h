@@ -109,6 +109,37 @@ hipError_t launch_row_topk(const float* rows, int64_t row_stride, const int* qli
                            int nq, const int* qpos, const int* qfirst, int q_start, int topk, int L,
                            int* out_idx, float* out_score, hipStream_t s);
 
+// Exact top-k of a few long score rows, each row split over `nchunk`
+// workgroups of `chunk_len` entries (recovery and the full rescore): three
+// radix passes over the rows find each row's k-th largest key, an emission
+// pass keeps the entries above it and the lowest-position entries equal to
+// it, and one workgroup per row sorts the kept entries.  Same result as
+// launch_row_topk.
+struct RowSelArgs {
+  const float* rows;
+  int64_t row_stride;
+  const int* qlist;    // entry e is query qlist[e] (or q_offset + e)
+  int q_offset;
+  int nq;
+  const int* qpos;
+  const int* qfirst;
+  int q_start;
+  int topk;
+  int L;
+  int nchunk;          // workgroups per row
+  int chunk_len;       // entries per workgroup (a multiple of 1024)
+  void* scratch;       // row_select_scratch_bytes(nq, nchunk, topk) bytes, 256-byte aligned
+  int* out_idx;
+  float* out_score;
+};
+
+hipError_t launch_row_select_split(const RowSelArgs& a, hipStream_t s);
+size_t row_select_scratch_bytes(int nrows, int nchunk, int topk);
+int row_select_max_chunks(int64_t L);
+// Chunking of rows of up to maxctx entries for nq rows (nchunk <= row_select_max_chunks(L)).
+void row_select_chunks(int nq, int64_t maxctx, int64_t L, int& nchunk, int& chunk_len);
+constexpr int kRowSplitMaxRows = 128;  // more rows than this fill the GPU one workgroup per row
+
 // LDS bytes cand_select needs for this cap / k (the host checks the limit).
 size_t cand_select_lds_bytes(int cap, int topk);
 

@@ -464,4 +464,323 @@ hipError_t launch_row_topk(const float* rows, int64_t row_stride, const int* qli
   return hipGetLastError();
 }
 
+// ----------------------------------------------------------------- split rows
+
+// Top-k of a few long rows (recovery of the flagged queries, the full
+// rescore in passes of rows): one workgroup per row would leave most of the
+// chip idle, so each row is split into `nchunk` chunks of `chunk_len`
+// entries.  Three radix passes over the 32-bit order-preserving keys (digits
+// of 11, 11 and 10 bits) find the row's k-th largest key v: in each pass
+// every chunk's workgroup counts the digits of its entries that match the
+// prefix chosen so far into a histogram of its own, and one workgroup per row
+// sums the chunk histograms and picks the digit that holds the remaining
+// rank.  Emission then keeps every entry above v and, of the entries equal
+// to v, the lowest positions (the entries' rank by position among the ties
+// comes from the last pass's per-chunk counts of v), which is the tie rule;
+// a last workgroup per row sorts the kept entries by (score descending,
+// position ascending).  The result is a function of the row contents only.
+
+constexpr int kSplitThreads = 256;
+constexpr int kSplitBins = 2048;  // bins of the widest digit
+constexpr int kSplitUnroll = 8;   // loads in flight per thread
+
+struct SplitState {
+  uint32_t prefix;  // key bits chosen so far (after the last pass: v)
+  uint32_t pmask;   // the bits the prefix covers
+  int r;            // rank sought among the entries matching the prefix (1-based)
+  int mult;         // entries whose key matches the prefix
+  int need;         // min(k, ctx)
+  int nout;         // entries emitted
+  int pad[2];
+};
+
+struct SplitLayout {
+  size_t state, tiebase, hist, staging, total;
+};
+
+static size_t align256(size_t x) { return (x + 255) / 256 * 256; }
+
+static SplitLayout split_layout(int nrows, int nchunk, int topk) {
+  SplitLayout l{};
+  size_t off = 0;
+  l.state = off; off = align256(off + (size_t)nrows * sizeof(SplitState));
+  l.tiebase = off; off = align256(off + (size_t)nrows * nchunk * 4);
+  l.hist = off; off = align256(off + (size_t)nrows * nchunk * kSplitBins * 4);
+  l.staging = off; off = align256(off + (size_t)nrows * topk * 8);
+  l.total = off;
+  return l;
+}
+
+size_t row_select_scratch_bytes(int nrows, int nchunk, int topk) {
+  return split_layout(nrows, nchunk, topk).total;
+}
+
+int row_select_max_chunks(int64_t L) {
+  const int64_t c = (L + 16383) / 16384;
+  return (int)(c < 1 ? 1 : (c > 64 ? 64 : c));
+}
+
+void row_select_chunks(int nq, int64_t maxctx, int64_t L, int& nchunk, int& chunk_len) {
+  const int cmax = row_select_max_chunks(L);
+  int64_t target = (1024 + nq - 1) / (nq > 0 ? nq : 1);  // about 1,024 workgroups per pass
+  target = target < 1 ? 1 : (target > cmax ? cmax : target);
+  if (maxctx < 1) maxctx = 1;
+  int64_t len = (maxctx + target - 1) / target;
+  len = (len + 1023) / 1024 * 1024;
+  nchunk = (int)((maxctx + len - 1) / len);
+  chunk_len = (int)len;
+}
+
+template <int PASS>
+struct SplitPass {
+  static constexpr int SHIFT = PASS == 0 ? 21 : (PASS == 1 ? 10 : 0);
+  static constexpr int BINS = PASS == 2 ? 1024 : 2048;
+  static constexpr uint32_t DMASK = (uint32_t)BINS - 1u;
+};
+
+__device__ __forceinline__ int split_query(const RowSelArgs& a, int e) {
+  return a.qlist ? a.qlist[e] : a.q_offset + e;
+}
+
+// Digit histogram of chunk blockIdx.x of row blockIdx.y over the entries that
+// match the prefix of the earlier passes; written whole (zeros included).
+template <int PASS>
+__global__ void __launch_bounds__(kSplitThreads) split_hist_kernel(RowSelArgs a,
+                                                                   const SplitState* st,
+                                                                   uint32_t* hist) {
+  using P = SplitPass<PASS>;
+  __shared__ int lh[P::BINS];
+  const int c = blockIdx.x, e = blockIdx.y, tid = threadIdx.x;
+  const QRange rg = query_range(a.qpos, a.qfirst, a.q_start, a.L, split_query(a, e));
+  const int ctx = max(0, rg.hi - rg.lo + 1);
+  for (int b = tid; b < P::BINS; b += kSplitThreads) lh[b] = 0;
+  uint32_t prefix = 0u, pmask = 0u;
+  if constexpr (PASS > 0) {
+    prefix = st[e].prefix;
+    pmask = st[e].pmask;
+  }
+  __syncthreads();
+  const int64_t c0 = (int64_t)c * a.chunk_len;
+  const int64_t c1 = min<int64_t>(ctx, c0 + a.chunk_len);
+  const float* row = a.rows + (int64_t)e * a.row_stride + rg.lo;
+  // runs of equal digits per thread are added with one LDS atomic each (in
+  // the first pass most entries share a few digits)
+  uint32_t run_d = 0u;
+  int run_n = 0;
+  for (int64_t i0 = c0; i0 < c1; i0 += kSplitUnroll * kSplitThreads) {
+    uint32_t kk[kSplitUnroll];
+#pragma unroll
+    for (int u = 0; u < kSplitUnroll; ++u) {
+      const int64_t i = i0 + u * kSplitThreads + tid;
+      kk[u] = i < c1 ? score_key(row[i]) : 0u;
+    }
+#pragma unroll
+    for (int u = 0; u < kSplitUnroll; ++u) {
+      const int64_t i = i0 + u * kSplitThreads + tid;
+      if (i < c1 && (kk[u] & pmask) == prefix) {
+        const uint32_t d = (kk[u] >> P::SHIFT) & P::DMASK;
+        if (run_n > 0 && d != run_d) {
+          atomicAdd(&lh[run_d], run_n);
+          run_n = 0;
+        }
+        run_d = d;
+        ++run_n;
+      }
+    }
+  }
+  if (run_n > 0) atomicAdd(&lh[run_d], run_n);
+  __syncthreads();
+  uint32_t* out = hist + ((int64_t)e * a.nchunk + c) * kSplitBins;
+  for (int b = tid; b < P::BINS; b += kSplitThreads) out[b] = (uint32_t)lh[b];
+}
+
+// One workgroup per row: sums the chunk histograms and picks the digit that
+// holds the remaining rank.  After the last pass it also stores, per chunk,
+// how many entries equal to v the earlier chunks hold (the tie ranks).
+template <int PASS>
+__global__ void __launch_bounds__(kSplitThreads) split_pick_kernel(RowSelArgs a, SplitState* st,
+                                                                   const uint32_t* hist,
+                                                                   uint32_t* tiebase) {
+  using P = SplitPass<PASS>;
+  constexpr int BPT = P::BINS / kSplitThreads;  // bins per thread
+  __shared__ int wsum[kSplitThreads / kWave];
+  const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int r, need;
+  uint32_t prefix = 0u, pmask = 0u;
+  if constexpr (PASS == 0) {
+    const QRange rg = query_range(a.qpos, a.qfirst, a.q_start, a.L, split_query(a, e));
+    need = min(a.topk, max(0, rg.hi - rg.lo + 1));
+    r = need;
+  } else {
+    const SplitState s0 = st[e];
+    need = s0.need;
+    r = s0.r;
+    prefix = s0.prefix;
+    pmask = s0.pmask;
+  }
+  if (need == 0) {  // empty context (uniform): nothing to select
+    if (PASS == 0 && tid == 0) st[e] = SplitState{0u, 0u, 0, 0, 0, 0, {0, 0}};
+    return;
+  }
+  // thread t holds bins BINS-1 - (BPT t + j), j = 0 .. BPT-1: descending
+  int cnt[BPT];
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) cnt[j] = 0;
+  const uint32_t* h = hist + (int64_t)e * a.nchunk * kSplitBins;
+  for (int c = 0; c < a.nchunk; ++c) {
+#pragma unroll
+    for (int j = 0; j < BPT; ++j) cnt[j] += (int)h[(int64_t)c * kSplitBins + P::BINS - 1 - (BPT * tid + j)];
+  }
+  int tot = 0;
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) tot += cnt[j];
+  int above = wave_prefix_excl(tot);
+  if (lane == kWave - 1) wsum[wave] = above + tot;
+  __syncthreads();
+  for (int w = 0; w < wave; ++w) above += wsum[w];
+#pragma unroll
+  for (int j = 0; j < BPT; ++j) {
+    if (above < r && r <= above + cnt[j]) {  // exactly one thread and bin
+      const uint32_t digit = (uint32_t)(P::BINS - 1 - (BPT * tid + j));
+      SplitState ns;
+      ns.prefix = prefix | (digit << P::SHIFT);
+      ns.pmask = pmask | (P::DMASK << P::SHIFT);
+      ns.r = r - above;
+      ns.mult = cnt[j];
+      ns.need = need;
+      ns.nout = 0;
+      ns.pad[0] = ns.pad[1] = 0;
+      st[e] = ns;
+      if constexpr (PASS == 2) {
+        uint32_t acc = 0u;
+        for (int c = 0; c < a.nchunk; ++c) {
+          tiebase[(int64_t)e * a.nchunk + c] = acc;
+          acc += h[(int64_t)c * kSplitBins + digit];
+        }
+      }
+    }
+    above += cnt[j];
+  }
+}
+
+// Emission: chunk blockIdx.x of row blockIdx.y appends its entries above v
+// and its kept ties (rank by position < the remaining rank) to the row's
+// staging list, in any order.
+__global__ void __launch_bounds__(kSplitThreads) split_emit_kernel(RowSelArgs a, SplitState* st,
+                                                                   const uint32_t* hist,
+                                                                   const uint32_t* tiebase,
+                                                                   uint2* staging) {
+  __shared__ int wcnt[kSplitThreads / kWave];
+  const int c = blockIdx.x, e = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int need = st[e].need;
+  if (need == 0) return;  // uniform
+  const uint32_t v = st[e].prefix;
+  const int rem = st[e].r;
+  const QRange rg = query_range(a.qpos, a.qfirst, a.q_start, a.L, split_query(a, e));
+  const int ctx = max(0, rg.hi - rg.lo + 1);
+  const int64_t c0 = (int64_t)c * a.chunk_len;
+  const int64_t c1 = min<int64_t>(ctx, c0 + a.chunk_len);
+  if (c0 >= c1) return;  // uniform
+  const float* row = a.rows + (int64_t)e * a.row_stride + rg.lo;
+  // entries equal to v in this chunk (the last pass's digit of v) and in the
+  // chunks before it
+  const uint32_t ties = hist[((int64_t)e * a.nchunk + c) * kSplitBins + (v & SplitPass<2>::DMASK)];
+  const int tb = (int)tiebase[(int64_t)e * a.nchunk + c];
+  const bool ordered = ties > 0u && tb < rem;  // some tie of this chunk may be kept (uniform)
+  uint2* dst = staging + (int64_t)e * a.topk;
+  int* nout = &st[e].nout;
+  const uint64_t lt = lane == 0 ? 0ull : (~0ull >> (64 - lane));
+  auto emit = [&](bool keep, uint32_t kk, int64_t i) {
+    const uint64_t mk = __ballot(keep);
+    if (mk == 0ull) return;  // uniform over the wave
+    int base = 0;
+    if (lane == 0) base = atomicAdd(nout, __popcll(mk));
+    base = __shfl(base, 0);
+    if (keep) {
+      const int slot = base + __popcll(mk & lt);
+      if (slot < a.topk) dst[slot] = make_uint2(kk, (uint32_t)(rg.lo + i));  // exactly need qualify
+    }
+  };
+  if (!ordered) {
+    for (int64_t i0 = c0; i0 < c1; i0 += kSplitUnroll * kSplitThreads) {
+      uint32_t kk[kSplitUnroll];
+#pragma unroll
+      for (int u = 0; u < kSplitUnroll; ++u) {
+        const int64_t i = i0 + u * kSplitThreads + tid;
+        kk[u] = i < c1 ? score_key(row[i]) : 0u;
+      }
+#pragma unroll
+      for (int u = 0; u < kSplitUnroll; ++u) {
+        const int64_t i = i0 + u * kSplitThreads + tid;
+        emit(i < c1 && kk[u] > v, kk[u], i);
+      }
+    }
+    return;
+  }
+  // Ties of this chunk may be kept: walk the chunk in position order, 256
+  // entries a round, ranking the ties by position.
+  int run = tb;  // ties before the current round
+  for (int64_t i0 = c0; i0 < c1; i0 += kSplitThreads) {
+    const int64_t i = i0 + tid;
+    const bool ok = i < c1;
+    const uint32_t kk = ok ? score_key(row[i]) : 0u;
+    const bool eq = ok && kk == v;
+    const uint64_t me = __ballot(eq);
+    if (lane == 0) wcnt[wave] = __popcll(me);
+    __syncthreads();
+    int before = run;
+    for (int w = 0; w < wave; ++w) before += wcnt[w];
+    int total = 0;
+#pragma unroll
+    for (int w = 0; w < kSplitThreads / kWave; ++w) total += wcnt[w];
+    const int rank = before + __popcll(me & lt);
+    emit((ok && kk > v) || (eq && rank < rem), kk, i);
+    run += total;
+    __syncthreads();  // wcnt is rewritten by the next round
+  }
+}
+
+// One workgroup per row: order the kept entries and write the output row.
+__global__ void __launch_bounds__(kSelThreads) split_sort_kernel(RowSelArgs a, const SplitState* st,
+                                                                 const uint2* staging) {
+  __shared__ SortScratch ss;
+  __shared__ uint32_t sk[2][kMaxRounds * kSelThreads];
+  __shared__ uint32_t sp[2][kMaxRounds * kSelThreads];
+  const int e = blockIdx.x, tid = threadIdx.x;
+  const int q = split_query(a, e);
+  const int need = st[e].need;
+  const uint2* src = staging + (int64_t)e * a.topk;
+  for (int i = tid; i < need; i += kSelThreads) {
+    const uint2 x = src[i];
+    sk[0][i] = x.x;
+    sp[0][i] = x.y;
+  }
+  __syncthreads();
+  sort_and_emit(sk[0], sp[0], sk[1], sp[1], need, a.topk, a.L, false,
+                a.out_idx + (int64_t)q * a.topk,
+                a.out_score ? a.out_score + (int64_t)q * a.topk : nullptr, ss);
+}
+
+hipError_t launch_row_select_split(const RowSelArgs& a, hipStream_t s) {
+  if (a.nq <= 0) return hipSuccess;
+  if (a.topk > kMaxRounds * kSelThreads || a.nchunk < 1 || a.chunk_len < 1) return hipErrorInvalidValue;
+  const SplitLayout l = split_layout(a.nq, a.nchunk, a.topk);
+  uint8_t* ws = static_cast<uint8_t*>(a.scratch);
+  SplitState* st = reinterpret_cast<SplitState*>(ws + l.state);
+  uint32_t* tiebase = reinterpret_cast<uint32_t*>(ws + l.tiebase);
+  uint32_t* hist = reinterpret_cast<uint32_t*>(ws + l.hist);
+  uint2* staging = reinterpret_cast<uint2*>(ws + l.staging);
+  const dim3 chunks((unsigned)a.nchunk, (unsigned)a.nq), rows((unsigned)a.nq);
+  const dim3 blk(kSplitThreads);
+  hipLaunchKernelGGL(split_hist_kernel<0>, chunks, blk, 0, s, a, st, hist);
+  hipLaunchKernelGGL(split_pick_kernel<0>, rows, blk, 0, s, a, st, hist, tiebase);
+  hipLaunchKernelGGL(split_hist_kernel<1>, chunks, blk, 0, s, a, st, hist);
+  hipLaunchKernelGGL(split_pick_kernel<1>, rows, blk, 0, s, a, st, hist, tiebase);
+  hipLaunchKernelGGL(split_hist_kernel<2>, chunks, blk, 0, s, a, st, hist);
+  hipLaunchKernelGGL(split_pick_kernel<2>, rows, blk, 0, s, a, st, hist, tiebase);
+  hipLaunchKernelGGL(split_emit_kernel, chunks, blk, 0, s, a, st, hist, tiebase, staging);
+  hipLaunchKernelGGL(split_sort_kernel, rows, dim3(kSelThreads), 0, s, a, st, staging);
+  return hipGetLastError();
+}
+
 }  // namespace hk

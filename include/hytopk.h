@@ -55,7 +55,7 @@
  *   * Supported in this version: 1 <= H <= 64 (heads beyond a multiple of 8
  *     are zero-padded; H <= 8 uses a narrow tile); d in {64, 128} for bf16,
  *     d = 128 for FP8 E4M3 and the MX formats (the backward included);
- *     1 <= k <= 2048; L < 2^31; cap <= 16384 and
+ *     1 <= k <= 2048; L, n, q_start < 2^31; cap <= 16384 and
  *     m_max <= 16384.  Other shapes return HYTOPK_EUNSUPPORTED.
  */
 #ifndef HYTOPK_H_
@@ -101,8 +101,8 @@ typedef enum {
  * Replay and backward take explicit indices and ignore both arrays. */
 typedef struct {
   int64_t L;        /* number of keys */
-  int64_t n;        /* number of queries */
-  int64_t q_start;  /* position of query 0 when q_pos is NULL (q_start + n <= L) */
+  int64_t n;        /* number of queries (< 2^31) */
+  int64_t q_start;  /* position of query 0 when q_pos is NULL (q_start + n <= L; < 2^31) */
   int32_t H;        /* indexer heads */
   int32_t d;        /* head dimension */
   int32_t k;        /* keys kept per query */
@@ -126,7 +126,8 @@ typedef struct {
   int32_t cap;          /* 6 * k */
   int32_t max_recover;  /* 64 */
   int32_t force_path;   /* HYTOPK_PATH_AUTO */
-  int32_t rows_chunk;   /* rows rescored per pass in the full rescore: min(n, max(max_recover, 2^29 / L)) */
+  int32_t rows_chunk;   /* rows of the score-row buffer: queries rescored per pass by recovery
+                           and the full rescore; min(n, max(1, max_recover)) (L * 4 bytes each) */
 } hytopk_params;
 
 /* What one hytopk_select call did (host struct, filled when non-NULL).

@@ -49,16 +49,24 @@ def test_workspace_sizes_match_the_worked_example(lib):
     # the conventional table: 8192 x 1,048,576 fp32 = 32 GiB per layer
     assert lib.hytopk_baseline_workspace(ctypes.byref(p)) == 32 << 30
     ws = lib.hytopk_select_workspace(ctypes.byref(p), None)
-    # candidates at cap = 6k: 8192 x 12288 x 8 bytes, plus the recovery rows
-    assert ws >= 8192 * 12288 * 8
-    assert ws < 4 << 30
+    # candidates at cap = 6k: 8192 x 12288 x 8 bytes (768 MiB), plus the
+    # recovery rows (max_recover = 64 rows of 2^20 fp32 scores: 256 MiB) and
+    # the split row top-k's scratch; the score table (32 GiB) is what the
+    # method avoids
+    cand, rows = 8192 * 12288 * 8, 64 * (1 << 20) * 4
+    assert cand + rows <= ws < int(1.1 * (1 << 30))
     assert ws % 256 == 0
+    # the rows buffer follows rows_chunk
+    prm = hk.Params(rows_chunk=16)
+    ws16 = lib.hytopk_select_workspace(ctypes.byref(p), ctypes.byref(prm))
+    assert cand + 16 * (1 << 20) * 4 <= ws16 < ws - 48 * (1 << 20) * 4 + (1 << 20)
 
 
 @pytest.mark.parametrize("kw,code", [
     (dict(n=0), -1), (dict(q_start=(1 << 20) - 8191), -1), (dict(k=0), -1),
     (dict(k=4097), -2), (dict(H=65), -2), (dict(d=96), -2), (dict(dtype=1, d=64), -2),
     (dict(dtype=7), -1), (dict(L=1 << 31, q_start=(1 << 31) - 8192), -2),
+    (dict(n=1 << 31, q_start=0, L=(1 << 31) - 1, q_pos=0x1000), -2),  # q_pos: no q_start + n check
 ])
 def test_invalid_problems_are_rejected_before_any_launch(lib, kw, code):
     p = _prob(**kw)
