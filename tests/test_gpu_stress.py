@@ -2,24 +2,36 @@
 H = 64, d = 128, k = 2,048, bf16): clustered keys with planted queries that
 overflow the candidate buffer or get fewer than k candidates.
 
-stress_a plants 32 + 16 failures (the recovery path), stress_b 96 + 32
-(more than 64: the full rescore).  The GPU's failure counts by kind must equal
-the planted groups, which the oracle's threshold model predicts to fail with a
-margin of at least 1,024 candidates.  Other queries may fail too (neighbours of
-the under-k run share its sample positions); every flagged query beyond the
-planted groups must be one the oracle's model also fails, and queries the
-model decides with a clear margin must agree with the GPU.  The recovered
-queries must match the oracle; the result must equal the score-table baseline
-bit for bit."""
+stress_a plants 32 overflowing + 16 under-k queries (48 <= 64: recovery),
+stress_b 96 + 32 (more than 64: the full rescore).  What is asserted:
+
+* the GPU's overflow count equals the planted overflow group, and its under-k
+  count is at least the planted under-k run (neighbours of the run share its
+  sample positions and may fall short of k as well);
+* every planted query is flagged, and the oracle's threshold model predicts
+  its failure, of the planted kind, with a margin of at least 1,024
+  candidates;
+* every flagged query beyond the planted groups is one the oracle's model
+  also fails, or one the model decides within a small margin (fewer than 64
+  candidates from cap or from k, or 8 or more scores within 1e-6 of tau, where
+  fp32 and fp64 may round either way); its margin is reported;
+* queries the model decides with a clear margin agree with the GPU;
+* every flagged query and a sample of ordinary ones match the oracle under
+  the float comparators, and the whole result equals the score-table
+  baseline bit for bit.
+"""
 import numpy as np
 import pytest
 import torch
 
 import datagen
 import oracle
-from gpu_util import assert_float_row, oracle_rows, say, to_device
+from gpu_util import assert_float_row, say, to_device
 
 pytestmark = pytest.mark.gpu
+
+ROBUST_MARGIN = 64   # candidates
+ROBUST_NEAR = 8      # scores within 1e-6 of tau
 
 
 @pytest.fixture(scope="module")
@@ -29,6 +41,12 @@ def hk():
     return m
 
 
+def _robust(p) -> bool:
+    return min(abs(p["margin_cap"]), abs(p["margin_k"])) >= ROBUST_MARGIN and \
+        p["near_tau"] < ROBUST_NEAR
+
+
+@pytest.mark.timeout(900)
 @pytest.mark.parametrize("name,path", [("stress_a", 0), ("stress_b", 1)])
 def test_stress_paths(hk, name, path):
     say(f"{name}: generating inputs")
@@ -38,33 +56,48 @@ def test_stress_paths(hk, name, path):
     say(f"{name}: hytopk_select")
     idx, sc, st = hk.select(dv["q"], dv["k"], dv["w"], inp.k, with_stats=True)
     torch.cuda.synchronize()
-    say(f"{name}: stats {st}")
+    say(f"{name}: stats " + str({k: v for k, v in st.items() if k != "failed"}))
     failed = np.array(st["failed"], dtype=np.int64)
     planted = set(over.tolist()) | set(under.tolist())
-    assert len(failed) == st["n_failed"] == st["n_overflow"] + st["n_underk"]
-    assert planted <= set(failed.tolist()), "a planted query was not flagged"
-    assert st["path"] == path
-    extra = sorted(set(failed.tolist()) - planted)
-    say(f"{name}: {len(failed)} flagged, {len(extra)} beyond the planted groups: {extra}")
-    # oracle: every flagged query beyond the planted groups, a sample of the
-    # planted ones, neighbours of the under-k run and a few ordinary queries
-    rng = np.random.default_rng(11)
-    check = list(under[:12]) + list(rng.choice(over, size=min(12, over.size), replace=False)) + extra
-    check += [int(under[0]) - 1, int(under[-1]) + 1, 0, inp.n - 1]
-    check = np.array(sorted(set(int(c) for c in check)))
-    say(f"{name}: oracle rows for {check.size} queries")
-    rows = oracle_rows(inp, check)
-    pred = oracle.predict_paths(rows, inp.k, inp.L, cap=6 * inp.k)
-    idx_n, sc_n = idx.cpu().numpy(), sc.cpu().numpy()
     flagged = set(failed.tolist())
+    assert len(failed) == st["n_failed"] == st["n_overflow"] + st["n_underk"]
+    assert st["n_overflow"] == over.size
+    assert st["n_underk"] >= under.size
+    assert planted <= flagged, "a planted query was not flagged"
+    assert st["path"] == path
+    extra = sorted(flagged - planted)
+    say(f"{name}: {len(failed)} flagged, {len(extra)} beyond the planted groups: {extra}")
+
+    # oracle: every flagged query, neighbours of the under-k run and a few
+    # ordinary queries
+    rng = np.random.default_rng(11)
+    check = set(flagged) | {int(under[0]) - 1, int(under[-1]) + 1, 0, inp.n - 1}
+    check |= set(int(c) for c in rng.choice(inp.n, size=8, replace=False))
+    check = np.array(sorted(check))
+    say(f"{name}: oracle rows for {check.size} queries")
+    dec = oracle.Decoded(inp)
+    idx_n, sc_n = idx.cpu().numpy(), sc.cpu().numpy()
+    model_over = model_under = 0
     for r, i in enumerate(check):
-        p = pred["per_query"][r]
-        robust = min(abs(p["margin_cap"]), abs(p["margin_k"])) >= 64 and p["near_tau"] < 8
-        if robust:
-            assert p["fail"] == (i in flagged), (i, p)
+        i = int(i)
+        row = oracle.score_row(dec, i)
+        p = oracle.predict_row(row, inp.k, inp.L, cap=6 * inp.k)
+        if i in flagged:
+            model_over += p["overflow"]
+            model_under += p["underk"]
         if i in planted:
-            assert p["fail"] and min(abs(p["margin_cap"]), abs(p["margin_k"])) >= 1024, (i, p)
-        assert_float_row(inp.L - inp.n + int(i), inp.k, rows[r], idx_n[i], sc_n[i], f"{name} q{i}")
+            assert p["fail"] and p["overflow"] == (i in set(over.tolist())), (i, p)
+            assert min(abs(p["margin_cap"]), abs(p["margin_k"])) >= 1024, (i, p)
+        elif i in flagged:
+            say(f"{name}: extra flagged q{i}: model fail={p['fail']} cnt={p['cnt']} "
+                f"margin_cap={p['margin_cap']} margin_k={p['margin_k']} near_tau={p['near_tau']}")
+            assert p["fail"] or not _robust(p), (i, p)
+        if _robust(p):
+            assert p["fail"] == (i in flagged), (i, p)
+        assert_float_row(inp.L - inp.n + i, inp.k, row, idx_n[i], sc_n[i], f"{name} q{i}")
+        if r % 32 == 31:
+            say(f"{name}: {r + 1} of {check.size} queries verified")
+    say(f"{name}: model among flagged: {model_over} overflow, {model_under} under-k")
     say(f"{name}: baseline (score table) for bitwise equality")
     bidx, bsc = hk.baseline_select(dv["q"], dv["k"], dv["w"], inp.k)
     torch.cuda.synchronize()
