@@ -15,7 +15,7 @@ __all__ = [
     "Problem", "Params", "Stats", "load_library", "library_path", "select", "replay",
     "baseline_select", "select_workspace_bytes", "baseline_workspace_bytes", "HytopkError",
     "EXPORTS", "BF16", "FP8_E4M3", "MXFP8_E4M3", "MXFP4_E2M1", "PATH_AUTO", "PATH_ROWS_ALL", "trace_enable", "trace_read",
-    "backward", "backward_workspace_bytes",
+    "backward", "backward_workspace_bytes", "select_noalloc", "NOALLOC_SCRATCH_BYTES",
 ]
 
 BF16, FP8_E4M3, MXFP8_E4M3, MXFP4_E2M1 = 0, 1, 2, 3
@@ -25,7 +25,9 @@ EXPORTS = (
     "hytopk_select_workspace", "hytopk_baseline_workspace", "hytopk_select", "hytopk_replay",
     "hytopk_baseline_select", "hytopk_backward_workspace", "hytopk_backward",
     "hytopk_status_string", "hytopk_last_error", "hytopk_trace_enable", "hytopk_trace_read",
+    "hytopk_select_noalloc",
 )
+NOALLOC_SCRATCH_BYTES = 64 << 20  # HYTOPK_NOALLOC_SCRATCH_BYTES
 
 
 class Problem(ctypes.Structure):
@@ -88,6 +90,9 @@ def load_library():
     lib.hytopk_select.argtypes = [P(Problem), P(Params), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp,
                                   P(Stats)]
     lib.hytopk_select.restype = ctypes.c_int
+    lib.hytopk_select_noalloc.argtypes = [P(Problem), P(Params), vp, vp, vp, vp, vp, vp, vp, vp,
+                                          P(Stats)]
+    lib.hytopk_select_noalloc.restype = ctypes.c_int
     lib.hytopk_replay.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp, vp, vp]
     lib.hytopk_replay.restype = ctypes.c_int
     lib.hytopk_baseline_select.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -234,6 +239,31 @@ def select(q, k, w, topk: int, *, q_scale=None, k_scale=None, q_start=None, para
     _check(lib.hytopk_select(ctypes.byref(prob), ctypes.byref(prm) if prm else None, _ptr(q),
                              _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w), _ptr(idx), _ptr(score),
                              _ptr(workspace), workspace.numel(), _stream(q), ctypes.byref(st)))
+    if not with_stats:
+        return idx, score
+    d = st.as_dict()
+    d["failed"] = [failed_buf[i] for i in range(min(st.n_failed, int(prob.n)))]
+    return idx, score, d
+
+
+def select_noalloc(q, k, w, topk: int, out, *, q_scale=None, k_scale=None, q_start=None,
+                   params=None, q_pos=None, q_first=None, fmt=None, with_stats: bool = False):
+    """hytopk_select_noalloc: select into the caller's ``out`` = (idx, score)
+    tensors with the library's static scratch as workspace (no allocation on
+    the device).  Returns ``out`` and, with ``with_stats``, the stats dict."""
+    lib = load_library()
+    prob = _problem(q, k, w, topk, q_start, q_pos, q_first, fmt)
+    prm = _params(params)
+    idx, score = out
+    st = Stats()
+    failed_buf = None
+    if with_stats:
+        failed_buf = (ctypes.c_int32 * int(prob.n))()
+        st.failed_queries = ctypes.cast(failed_buf, ctypes.POINTER(ctypes.c_int32))
+        st.failed_capacity = int(prob.n)
+    _check(lib.hytopk_select_noalloc(ctypes.byref(prob), ctypes.byref(prm) if prm else None,
+                                     _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w),
+                                     _ptr(idx), _ptr(score), _stream(q), ctypes.byref(st)))
     if not with_stats:
         return idx, score
     d = st.as_dict()

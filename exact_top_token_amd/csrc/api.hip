@@ -14,6 +14,11 @@
 #include "hytopk.h"
 #include "launch.h"
 
+constexpr size_t kNoAllocBytes = size_t(64) << 20;
+static_assert(kNoAllocBytes == HYTOPK_NOALLOC_SCRATCH_BYTES, "header and library disagree");
+// The workspace of hytopk_select_noalloc (see scratch_address below).
+static __device__ __align__(256) uint8_t scratch[kNoAllocBytes];
+
 namespace {
 
 thread_local std::string g_err;
@@ -312,6 +317,33 @@ int rows_path(const hytopk_problem* p, const hk::ScoreArgs& base, const int* qli
   return HYTOPK_OK;
 }
 
+// Library-owned workspace of hytopk_select_noalloc: one copy per GPU the
+// library runs on, held until the process ends.  Host code never passes the
+// array's name to a kernel or a copy (on the host it is a stand-in, not a
+// device address); it uses the per-device address hipGetSymbolAddress gives.
+std::mutex g_scratch_mu;
+std::map<int, void*> g_scratch_ptr;  // device ordinal -> device address of `scratch`
+
+// Device address of this device's `scratch`, looked up on the first call on
+// each device (with that device current).
+int scratch_address(void** out) {
+  int dev = 0;
+  HK_HIP(hipGetDevice(&dev), "hipGetDevice");
+  std::lock_guard<std::mutex> g(g_scratch_mu);
+  auto it = g_scratch_ptr.find(dev);
+  if (it != g_scratch_ptr.end()) {
+    *out = it->second;
+    return HYTOPK_OK;
+  }
+  void* ptr = nullptr;
+  HK_HIP(hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)), "hipGetSymbolAddress(scratch)");
+  if (!ptr || reinterpret_cast<uintptr_t>(ptr) % kAlign)
+    return fail(HYTOPK_EHIP, "static scratch has no usable device address");
+  g_scratch_ptr[dev] = ptr;
+  *out = ptr;
+  return HYTOPK_OK;
+}
+
 }  // namespace
 
 extern "C" {
@@ -485,6 +517,29 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
     stats->path = path;
   }
   return HYTOPK_OK;
+}
+
+int hytopk_select_noalloc(const hytopk_problem* p, const hytopk_params* prm, const void* q,
+                          const void* q_scale, const void* k, const void* k_scale, const float* w,
+                          int32_t* out_idx, float* out_score, void* stream, hytopk_stats* stats) {
+  g_err.clear();
+  int rc = check_problem(p);
+  if (rc) return rc;
+  Params r = resolve(p, prm);
+  if ((rc = check_params(p, r))) return rc;
+  const size_t need = layout(p, r).total;
+  if (need > kNoAllocBytes) {
+    char msg[160];
+    std::snprintf(msg, sizeof msg,
+                  "problem needs %zu bytes of workspace, more than the %zu-byte static scratch "
+                  "(use hytopk_select with a workspace, or a smaller rows_chunk / cap)",
+                  need, kNoAllocBytes);
+    return fail(HYTOPK_EWORKSPACE, msg);
+  }
+  void* ws = nullptr;
+  if ((rc = scratch_address(&ws))) return rc;
+  return hytopk_select(p, prm, q, q_scale, k, k_scale, w, out_idx, out_score, ws, kNoAllocBytes,
+                       stream, stats);
 }
 
 int hytopk_replay(const hytopk_problem* p, const void* q, const void* q_scale, const void* k,

@@ -162,6 +162,26 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm,
                   const float* w, int32_t* out_idx, float* out_score,
                   void* workspace, size_t workspace_bytes, void* stream, hytopk_stats* stats);
 
+/* Bytes of the library's static scratch used by hytopk_select_noalloc. */
+#define HYTOPK_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+/* hytopk_select for callers that cannot allocate device memory (code under
+ * stream capture, tight serving loops, harnesses that forbid allocation):
+ * the same arguments and results without the workspace, which is taken from a
+ * static device buffer of HYTOPK_NOALLOC_SCRATCH_BYTES owned by the library
+ * (one per GPU it runs on, held until the process ends).  The call allocates
+ * nothing.  A problem whose hytopk_select_workspace exceeds the buffer
+ * returns HYTOPK_EWORKSPACE before any launch (the rows buffer, rows_chunk *
+ * L * 4 bytes, and the candidate buffer, n * cap * 8 bytes, dominate; lower
+ * rows_chunk or cap to fit).  Every call on a GPU shares that GPU's buffer
+ * and leaves its contents behind: calls that overlap on one GPU (on different
+ * streams or threads) race and must be serialised by the caller.  Like
+ * hytopk_select it synchronises its stream once. */
+int hytopk_select_noalloc(const hytopk_problem* p, const hytopk_params* prm,
+                          const void* q, const void* q_scale, const void* k, const void* k_scale,
+                          const float* w, int32_t* out_idx, float* out_score, void* stream,
+                          hytopk_stats* stats);
+
 /* Selection replay: out_score[i][j] = I(q_start + i, idx[i][j]) for the saved
  * indices idx [n][k] int32 (HyScale explainer, selection-replay paragraph).
  * An index outside [0, L) is padding and gives -inf (never dereferenced);
