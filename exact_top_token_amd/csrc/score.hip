@@ -81,6 +81,13 @@ score_tile_kernel(ScoreArgs a) {
   __shared__ int s_minlo[kWaves];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4;
+  // XOR swizzle of a key row's 16-byte chunks in a stage.  A B-fragment read
+  // (16 bytes per lane) is served 16 lanes -- 16 consecutive keys of one lane
+  // group -- at a time by 64 four-byte banks, so the 16 keys must land on 16
+  // distinct 16-byte bank groups: key kk's row starts at group (kk * NCH) % 16,
+  // and the swizzle adds the key bits above that, (kk / (16 / NCH)) % NCH.
+  // (For 16-chunk bf16 rows this is kk % 16.)
+  auto swz = [](int kk) { return (kk / (16 / NCH)) & (NCH - 1); };
   const int group = blockIdx.x / a.nsplit, split = blockIdx.x % a.nsplit;
   const int e0 = group * kGroupQ + wave * 2;
   const int ea = e0 < a.nq ? e0 : -1;
@@ -114,10 +121,10 @@ score_tile_kernel(ScoreArgs a) {
 
   // DMA layout: load p of wave w fills 1 KB block p * kWaves + w of a stage; its
   // lane j lands on key kk = block * KPB + j / NCH, 16-byte slot j % NCH,
-  // and fetches chunk (slot ^ (kk % NCH)) of that key: the swizzle the B
-  // fragment reads undo.  kk % NCH does not depend on p.
+  // and fetches chunk (slot ^ swz(kk)) of that key: the swizzle the B
+  // fragment reads undo.  swz(kk) does not depend on p.
   const int dma_kk = wave * KPB + lane / NCH;
-  const int dma_c = ((lane % NCH) ^ (dma_kk & (NCH - 1))) * 16;
+  const int dma_c = ((lane % NCH) ^ swz(dma_kk)) * 16;
   const int full_tiles = (a.L - kb) / TK;  // tiles that lie entirely below L
   // Full tiles (all but the last one or two) take a per-lane constant offset
   // from a scalar tile base, and the LDS destination is wave-uniform, so
@@ -202,13 +209,13 @@ score_tile_kernel(ScoreArgs a) {
         const uint8_t* krow = tb + kt * RBYTES;
         if constexpr (F::FB == 32) {  // E4M3: two 16-byte chunks
           const int c0 = CPS * ks + F::chunk0(g), c1 = CPS * ks + F::chunk1(g);
-          const u32x4 lo = *reinterpret_cast<const u32x4*>(krow + ((c0 ^ (kt & (NCH - 1))) * 16));
-          const u32x4 hi = *reinterpret_cast<const u32x4*>(krow + ((c1 ^ (kt & (NCH - 1))) * 16));
+          const u32x4 lo = *reinterpret_cast<const u32x4*>(krow + ((c0 ^ swz(kt)) * 16));
+          const u32x4 hi = *reinterpret_cast<const u32x4*>(krow + ((c1 ^ swz(kt)) * 16));
           b[ks] = i32x8{(int)lo[0], (int)lo[1], (int)lo[2], (int)lo[3],
                         (int)hi[0], (int)hi[1], (int)hi[2], (int)hi[3]};
         } else {  // bf16 or E2M1: one 16-byte chunk (frag reads chunk g of its slice)
           const int c = CPS * ks + g;
-          b[ks] = F::frag(krow + ((c ^ (kt & (NCH - 1))) * 16) - 16 * g, g);
+          b[ks] = F::frag(krow + ((c ^ swz(kt)) * 16) - 16 * g, g);
         }
       }
       float s = qt.score(b, sb);
