@@ -5,6 +5,7 @@
 
 #include <algorithm>
 #include <cstdio>
+#include <cstdlib>
 #include <cstring>
 #include <map>
 #include <mutex>
@@ -266,6 +267,10 @@ hk::ScoreArgs score_args(const hytopk_problem* p, const void* q, const void* qs,
   a.qpos = p->q_pos;
   a.qfirst = p->q_first;
   a.H = p->H;
+  // Debug knob (determinism check): HYTOPK_REVERSE_KEY_WALK=1 makes the
+  // scoring kernels walk key tiles from last to first; results must not change.
+  const char* rev = std::getenv("HYTOPK_REVERSE_KEY_WALK");
+  a.reverse = (rev && rev[0] == '1') ? 1 : 0;
   return a;
 }
 

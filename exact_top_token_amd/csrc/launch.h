@@ -37,6 +37,7 @@ struct ScoreArgs {
   int cap;
   int nsplit;
   int split_len;
+  int reverse;         // 1: walk each launch entry's key tiles from last to first
 };
 
 hipError_t launch_score(const ScoreArgs& a, int d, int fmt, hipStream_t s);

@@ -148,9 +148,14 @@ score_tile_kernel(ScoreArgs a) {
       }
     }
   };
-  issue(0, t0);
-  if (1 < ntiles) issue(1, t1);
-  if (2 < ntiles) issue(2, t2);
+  // Walk position it scores key tile tile_of(it): ascending, or descending
+  // when the caller asks for the reversed walk (a determinism check: the
+  // candidates then reach the buffer in the opposite order, and the result,
+  // which depends only on the candidate multiset, must not change).
+  auto tile_of = [&](int it) { return a.reverse ? ntiles - 1 - it : it; };
+  issue(tile_of(0), t0);
+  if (1 < ntiles) issue(tile_of(1), t1);
+  if (2 < ntiles) issue(tile_of(2), t2);
 
   T qt;
   qt.load(a.q, a.w, a.q_scale, a.H, qa, qb, lin_lds[F::SCALED ? wave : 0]);
@@ -279,11 +284,12 @@ score_tile_kernel(ScoreArgs a) {
   // with tile it+3, score tile it.  Key scales are read before the refill
   // so that waiting for them never waits for the refill.
   auto step = [&](int it, const uint8_t* cur, uint8_t* refill) {
+    const int tl = tile_of(it);
     KeyScales ksc;
     if constexpr (F::SCALED) {
 #pragma unroll
       for (int cb = 0; cb < NCB; ++cb) {
-        const int key = min(kb + it * TK + cb * 16 + (lane & 15), a.L - 1);
+        const int key = min(kb + tl * TK + cb * 16 + (lane & 15), a.L - 1);
         if constexpr (FMT == kFP8) {
           ksc.f[cb] = static_cast<const float*>(a.k_scale)[key];
         } else {
@@ -299,8 +305,8 @@ score_tile_kernel(ScoreArgs a) {
       HK_WAIT_VM(F::SCALED ? NCB : 0);
     }
     __builtin_amdgcn_s_barrier();
-    if (it + 3 < ntiles) issue(it + 3, refill);
-    compute(it, cur, ksc);
+    if (it + 3 < ntiles) issue(tile_of(it + 3), refill);
+    compute(tl, cur, ksc);
   };
   for (int it = 0; it < ntiles; it += 4) {
     step(it, t0, t3);

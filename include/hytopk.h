@@ -236,6 +236,12 @@ int hytopk_backward(const hytopk_problem* p, const void* q, const void* q_scale,
 const char* hytopk_status_string(int status);
 const char* hytopk_last_error(void);  /* thread-local; "" when none */
 
+/* Debug knob (environment, read on every call): HYTOPK_REVERSE_KEY_WALK=1
+ * makes the scoring kernels of hytopk_select and hytopk_baseline_select walk
+ * each query group's key tiles from the last to the first.  Candidates then
+ * reach the buffer in a different order; the results are bitwise identical
+ * (selection depends only on the candidate multiset). */
+
 /* Kernel tracing.  While enabled, every launch the library makes is bracketed
  * by a pair of hipEvents recorded on the caller's stream, and the elapsed time
  * is accumulated per phase name ("sample_tau", "score_compact", "check",

@@ -183,3 +183,29 @@ def test_api_errors_do_not_launch(hk, tiny):
     with pytest.raises(hk.HytopkError) as e:
         hk.baseline_select(d["q"], d["k"], d["w"], inp.k, workspace=ws[1:])
     assert e.value.status == -3
+
+
+@pytest.mark.parametrize("shape", ["tiny", "one_split"])
+def test_reversed_key_walk_gives_the_same_bits(hk, tiny, shape, monkeypatch):
+    """The scoring kernel walks key tiles last-to-first under the
+    HYTOPK_REVERSE_KEY_WALK knob, so candidates reach the buffer in another
+    order (several key splits: staged flushes; one split: direct stores); the
+    selection, the scores and the candidate counts must not change."""
+    if shape == "tiny":
+        inp, d = tiny["inp"], tiny["dev"]
+    else:
+        inp = datagen.make_custom("rev", 12000, 8190, 8, 128, 64, dist="int", seed=5)
+        d = to_device(inp)
+    say(f"reversed key walk: {shape} L={inp.L} n={inp.n} H={inp.H} k={inp.k}")
+    monkeypatch.delenv("HYTOPK_REVERSE_KEY_WALK", raising=False)
+    idx0, sc0, st0 = hk.select(d["q"], d["k"], d["w"], inp.k, with_stats=True)
+    b0 = [_np(t) for t in hk.baseline_select(d["q"], d["k"], d["w"], inp.k)]
+    monkeypatch.setenv("HYTOPK_REVERSE_KEY_WALK", "1")
+    idx1, sc1, st1 = hk.select(d["q"], d["k"], d["w"], inp.k, with_stats=True)
+    b1 = [_np(t) for t in hk.baseline_select(d["q"], d["k"], d["w"], inp.k)]
+    torch.cuda.synchronize()
+    assert np.array_equal(_np(idx0), _np(idx1))
+    assert np.array_equal(_np(sc0).view(np.uint32), _np(sc1).view(np.uint32))
+    assert st0 == st1
+    assert np.array_equal(b0[0], b1[0]) and np.array_equal(b0[1].view(np.uint32), b1[1].view(np.uint32))
+    assert np.array_equal(b0[0], _np(idx0))
