@@ -157,6 +157,9 @@ int check_params(const hytopk_problem* p, const Params& r) {
     return fail(HYTOPK_EINVAL, "invalid threshold parameters");
   if (r.force_path != HYTOPK_PATH_AUTO && r.force_path != HYTOPK_PATH_ROWS_ALL)
     return fail(HYTOPK_EINVAL, "unknown force_path");
+  // the rows buffer (rows_chunk x L fp32) must stay far from size_t overflow
+  if (std::min<int64_t>(r.rows_chunk, p->n) * p->L > (int64_t(1) << 40))
+    return fail(HYTOPK_EUNSUPPORTED, "rows_chunk * L > 2^40");
   if (r.m_max > kMaxM) return fail(HYTOPK_EUNSUPPORTED, "m_max > 16384");
   if (r.cap > kMaxCap) return fail(HYTOPK_EUNSUPPORTED, "cap > 16384");
   if (hk::cand_select_lds_bytes(r.cap, p->k) > kLdsLimit)
