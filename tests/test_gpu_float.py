@@ -93,12 +93,12 @@ def test_glm1m_bf16(hk):
 
 
 def test_glm1m_fp8(hk):
-    _run_config(hk, "glm1m_fp8", 64, with_baseline=False)
+    _run_config(hk, "glm1m_fp8", 64, with_baseline=True)
 
 
 def test_glm1m_mxfp8(hk):
-    _run_config(hk, "glm1m_mxfp8", 32, with_baseline=False)
+    _run_config(hk, "glm1m_mxfp8", 64, with_baseline=True)
 
 
 def test_glm1m_mxfp4(hk):
-    _run_config(hk, "glm1m_mxfp4", 32, with_baseline=True)
+    _run_config(hk, "glm1m_mxfp4", 64, with_baseline=True)
