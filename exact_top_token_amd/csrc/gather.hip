@@ -206,6 +206,7 @@ hipError_t launch_replay(const ReplayArgs& a, int d, int fmt, hipStream_t s) {
 // ----------------------------------------------------------------- threshold
 
 constexpr int kSampleThreads = 256;  // 4 waves share one query's samples
+constexpr int kSampleDepth = 3;      // column blocks of gathers in flight per wave
 
 // One query per workgroup.  Row block rb of the A operand holds heads
 // 16 rb .. 16 rb + 15 of the query; output lane group g holds heads
@@ -242,18 +243,40 @@ __global__ void __launch_bounds__(kSampleThreads) sample_tau_kernel(SampleArgs a
   T qt;
   qt.load(a.q, a.w, a.q_scale, a.H, q, lin_lds[wave]);
 
-  for (int cb = wave; cb * 16 < mq; cb += kSampleThreads / kWave) {
-    const int j = cb * 16 + (lane & 15);
+  // Wave w scores column blocks w, w + 4, ... of 16 samples, with the
+  // gathers of the next kSampleDepth - 1 of its blocks in flight while it
+  // scores one (the gathers, served from L2 and beyond, are the latency to
+  // hide).  Blocks past the last one fetch nothing.
+  const int ncb = (mq + 15) / 16;
+  constexpr int kStride = kSampleThreads / kWave;
+  Frag buf[kSampleDepth][KS];
+  int sbuf[kSampleDepth][KS];
+  int kpos[kSampleDepth];
+  float ksc[kSampleDepth];
+  auto fetch = [&](int i, int slot) {  // the wave's i-th block into ring slot `slot`
+    const int j = (wave + i * kStride) * 16 + (lane & 15);
     const int pos = j < mq ? rg.lo + (int)(((int64_t)j * ctx) / mq) : -1;
-    Frag b[KS];
-    int sb[KS];
-    T::key(a.k, a.k_scale, pos, b, sb);
-    // The selection kernels' head-sum order: a sampled key's score is
-    // bit-identical to the score the fused kernel compares with tau, so the
-    // r sampled keys at or above tau always pass.
-    float s = qt.score(b, sb);
-    if constexpr (FMT == kFP8) s *= pos >= 0 ? static_cast<const float*>(a.k_scale)[pos] : 0.0f;
-    if (lane < 16 && j < mq) S[j] = s;
+    kpos[slot] = pos;
+    T::key(a.k, a.k_scale, pos, buf[slot], sbuf[slot]);
+    if constexpr (FMT == kFP8) ksc[slot] = pos >= 0 ? static_cast<const float*>(a.k_scale)[pos] : 0.0f;
+  };
+  const int nmine = wave < ncb ? (ncb - wave + kStride - 1) / kStride : 0;  // wave-uniform
+#pragma unroll
+  for (int d = 0; d < kSampleDepth - 1; ++d) fetch(d, d);
+  for (int i0 = 0; i0 < nmine; i0 += kSampleDepth) {
+#pragma unroll
+    for (int d = 0; d < kSampleDepth; ++d) {
+      const int i = i0 + d;
+      if (i >= nmine) break;  // wave-uniform
+      fetch(i + kSampleDepth - 1, (d + kSampleDepth - 1) % kSampleDepth);
+      // The selection kernels' head-sum order: a sampled key's score is
+      // bit-identical to the score the fused kernel compares with tau, so the
+      // r sampled keys at or above tau always pass.
+      float s = qt.score(buf[d], sbuf[d]);
+      if constexpr (FMT == kFP8) s *= ksc[d];
+      const int j = (wave + i * kStride) * 16 + (lane & 15);
+      if (lane < 16 && kpos[d] >= 0) S[j] = s;
+    }
   }
   __syncthreads();
   int rem, mult;

@@ -81,13 +81,24 @@ score_tile_kernel(ScoreArgs a) {
   __shared__ int s_minlo[kWaves];
 
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4;
-  // XOR swizzle of a key row's 16-byte chunks in a stage.  A B-fragment read
-  // (16 bytes per lane) is served 16 lanes -- 16 consecutive keys of one lane
-  // group -- at a time by 64 four-byte banks, so the 16 keys must land on 16
-  // distinct 16-byte bank groups: key kk's row starts at group (kk * NCH) % 16,
-  // and the swizzle adds the key bits above that, (kk / (16 / NCH)) % NCH.
-  // (For 16-chunk bf16 rows this is kk % 16.)
-  auto swz = [](int kk) { return (kk / (16 / NCH)) & (NCH - 1); };
+  // XOR swizzle of a key row's 16-byte chunks in a stage, so that B-fragment
+  // reads (16 bytes per lane) are free of LDS bank conflicts.  The LDS
+  // counters on gfx950 fit this model of such a read, and only this one
+  // among the lane groupings tried: 64 four-byte banks, eight lanes at a time,
+  // the lanes that agree in bits 0, 3 and 5 of the lane index (keys
+  // kk = lane % 16 of one parity and one half, in two adjacent lane groups).
+  // Those eight lanes must reach eight distinct 16-byte bank groups for
+  // every chunk pattern the formats read: chunk g (and 4 + g) of 8-chunk MX
+  // rows, 2g and 2g + 1 of per-token E4M3 rows, 4 ks + g of bf16 rows, g of
+  // E2M1 rows.  A bank simulation of this model gives zero conflicts for
+  // all of them with the swizzles below (and the counters read zero for the
+  // formats measured).
+  auto swz = [](int kk) {
+    if constexpr (NCH == 16) return kk & 15;
+    else if constexpr (NCH == 8) return (kk & 6) ^ ((kk >> 1) & 1);
+    else return (kk >> 1) & (NCH - 1);
+  };
+  static_assert(NCH == 4 || NCH == 8 || NCH == 16, "key rows of 4, 8 or 16 chunks");
   const int group = blockIdx.x / a.nsplit, split = blockIdx.x % a.nsplit;
   const int e0 = group * kGroupQ + wave * 2;
   const int ea = e0 < a.nq ? e0 : -1;
