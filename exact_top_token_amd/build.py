@@ -64,8 +64,10 @@ def build(verbose: bool = True) -> str:
     with cf.ThreadPoolExecutor(workers) as ex:
         list(ex.map(_run, jobs))
     tmp = LIB + ".tmp"
+    # -z defs: an unresolved symbol (say, a kernel whose host stub the
+    # compiler dropped) fails the link instead of the first load
     _run([cc, f"--offload-arch={ARCH}", "-shared", "-fPIC", "-o", tmp, *objs,
-          "-Wl,-rpath,/opt/rocm/lib"])
+          "-Wl,-rpath,/opt/rocm/lib", "-Wl,-z,defs"])
     os.replace(tmp, LIB)
     if verbose:
         print(f"built {LIB}")

@@ -212,6 +212,10 @@ int check_inputs(const hytopk_problem* p, const void* q, const void* qs, const v
   if (!q || !k || !w) return fail(HYTOPK_EINVAL, "q, k and w must be non-NULL");
   if (p->dtype != HYTOPK_BF16 && (!qs || !ks))
     return fail(HYTOPK_EINVAL, "fp8 and MX formats need q_scale and k_scale");
+  auto off = [](const void* x, uintptr_t a) { return reinterpret_cast<uintptr_t>(x) % a != 0; };
+  if (off(q, 16) || off(k, 16)) return fail(HYTOPK_EINVAL, "q and k must be 16-byte aligned");
+  if (off(w, 4) || off(qs, 4) || off(ks, 4))
+    return fail(HYTOPK_EINVAL, "w, q_scale and k_scale must be 4-byte aligned");
   return HYTOPK_OK;
 }
 

@@ -120,8 +120,8 @@ struct QueryTile {
         p = __builtin_fmaf(x, wf[rb][i], p);
       }
     }
-    const float t = p + __shfl_xor(p, 32);  // even + odd row blocks of this half
-    return t + __shfl_xor(t, 16);           // + the other half
+    const float t = add_lane_xor32(p);  // even + odd row blocks of this half
+    return add_lane_xor16(t);           // + the other half
   }
 };
 
@@ -206,21 +206,212 @@ hipError_t launch_replay(const ReplayArgs& a, int d, int fmt, hipStream_t s) {
 // ----------------------------------------------------------------- threshold
 
 constexpr int kSampleThreads = 256;  // 4 waves share one query's samples
-constexpr int kSampleDepth = 3;      // column blocks of gathers in flight per wave
+constexpr int kSampleWaves = kSampleThreads / kWave;
+constexpr int kSampleDepth = 3;      // scaled formats: column blocks of gathers in flight per wave
+constexpr int kSampleRing = 8192;    // bf16: bytes of staged key rows per wave
+
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
+// Reads N 16-byte chunks of a staged block in one asm block that also waits
+// for them.  The compiler does not see these reads, so it does not make
+// them wait for every direct-to-LDS load still in flight (its own analysis
+// cannot tell the ring's stages apart and would, serialising the ring); the
+// wait before them is explicit.  Outputs are early-clobber, and the asm
+// waits for its loads before it ends.
+template <int N>
+__device__ __forceinline__ void lds_read_chunks(const uint32_t (&ad)[N], u32x4 (&r)[N]) {
+  static_assert(N == 2 || N == 4, "two or four chunks");
+  if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1])
+        : "v"(ad[0]), "v"(ad[1])
+        : "memory");
+  }
+}
+
+// Loads samples j0 .. j0 + 15 of a query (positions P[j], j < mq; rows past
+// the samples load row `lo` and are never scored) into the wave's stage
+// `dst`: OPS direct-to-LDS loads of 1 KB (load p, lane l: key p * KPI + dkk,
+// byte offset dsw[p] in its row).
+template <int OPS, int KPI, int RBYTES>
+__device__ __forceinline__ void stage_sample_block(const uint8_t* k, const int* P, int j0, int mq,
+                                                   int lo, int dkk, const int (&dsw)[OPS],
+                                                   uint8_t* dst) {
+  // every position first, so that the LDS reads go out together
+  int rowpos[OPS];
+#pragma unroll
+  for (int p = 0; p < OPS; ++p) {
+    const int js = j0 + p * KPI + dkk;
+    rowpos[p] = js < mq ? P[js] : lo;
+  }
+#pragma unroll
+  for (int p = 0; p < OPS; ++p) lds_dma16(k + (int64_t)rowpos[p] * RBYTES + dsw[p], dst + p * 1024);
+}
+
+// bf16 samples: the sampled key rows reach the waves through LDS.
+// Direct-to-LDS loads fetch each row whole (16 consecutive lanes per row,
+// four lanes to each 64-byte piece), where loading the MFMA operand layout
+// straight from memory gives every lane its own 16-byte piece of a
+// different row: four times the address-unit work per byte, which bounded
+// the gathers (the address path stalled on the cache 62% of the time).
+// Wave w scores column blocks w, w + 4, ...; each wave owns a ring of
+// DEPTH stages, kSampleRing bytes, and waits for a stage's loads by count.
+// S[0 .. mq) first receives the sample positions (computed once, not per
+// load), then the scores; a block's entries are touched only by its wave.
+template <int RB4, int D>
+__device__ __forceinline__ void sample_scores_staged(const SampleArgs& a, const QueryTile<RB4, D, kBF16>& qt,
+                                                     QRange rg, int ctx, int mq, float* S) {
+  using F = Fmt<kBF16>;
+  using T = QueryTile<RB4, D, kBF16>;
+  constexpr int KS = T::KS, RBYTES = T::RBYTES, NCH = RBYTES / 16;
+  constexpr int CB_BYTES = 16 * RBYTES;  // a column block's 16 key rows
+  constexpr int DEPTH = kSampleRing / CB_BYTES;
+  constexpr int OPS = CB_BYTES / 1024;   // 1 KB loads per column block (= its vector-memory ops)
+  constexpr int KPI = 1024 / RBYTES;     // key rows per load
+  constexpr int SLOT = kSampleWaves * CB_BYTES;
+  static_assert(CB_BYTES % 1024 == 0 && DEPTH >= 2 && DEPTH <= 4, "stage ring shape");
+  __shared__ __attribute__((aligned(1024))) uint8_t ring_lds[DEPTH * SLOT];
+  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4;
+
+  // positions lo + floor(j * ctx / mq): thread t takes a run of consecutive
+  // j, one division for its first and the remainder carried from there
+  int* P = reinterpret_cast<int*>(S);
+  {
+    const int per = (mq + kSampleThreads - 1) / kSampleThreads;
+    const int j0 = tid * per, j1 = min(mq, j0 + per);
+    if (j0 < j1) {
+      const int dq = ctx / mq, dr = ctx % mq;
+      const int64_t n0 = (int64_t)j0 * ctx;
+      int pos = (int)(n0 / mq), rem = (int)(n0 % mq);
+      for (int j = j0; j < j1; ++j) {
+        P[j] = rg.lo + pos;
+        pos += dq;
+        rem += dr;
+        if (rem >= mq) { rem -= mq; ++pos; }
+      }
+    }
+  }
+  __syncthreads();
+
+  const int ncb = (mq + 15) / 16;
+  const int nmine = wave < ncb ? (ncb - wave + kSampleWaves - 1) / kSampleWaves : 0;  // wave-uniform
+  uint8_t* const ring0 = ring_lds + __builtin_amdgcn_readfirstlane(wave) * CB_BYTES;  // stage s: + s * SLOT
+  const int dkk = lane / NCH;
+  int dsw[OPS];  // the stage's swizzle: load p fetches this chunk of its row
+#pragma unroll
+  for (int p = 0; p < OPS; ++p) dsw[p] = 16 * ((lane % NCH) ^ key_swz<NCH>(p * KPI + dkk));
+  auto issue = [&](int i, int slot) {  // the wave's i-th block into ring slot `slot`
+    stage_sample_block<OPS, KPI, RBYTES>(a.k, P, (wave + i * kSampleWaves) * 16, mq, rg.lo, dkk, dsw,
+                                         ring0 + slot * SLOT);
+  };
+  // Straight-line body: loads run DEPTH - 1 blocks ahead unconditionally and
+  // the last round is scored whole (blocks past the wave's last one load row
+  // lo and store nothing: their samples lie past mq), so every block waits
+  // with the same count.
+#pragma unroll
+  for (int d = 0; d < DEPTH - 1; ++d) issue(d, d);
+  for (int i0 = 0; i0 < nmine; i0 += DEPTH) {
+#pragma unroll
+    for (int d = 0; d < DEPTH; ++d) {
+      const int i = i0 + d;
+      issue(i + DEPTH - 1, (d + DEPTH - 1) % DEPTH);
+      HK_WAIT_VM((DEPTH - 1) * OPS);  // block i's loads have landed
+      // lane (kt, g): chunk CPS ks + g of key kt, for each k-step
+      const int kt = lane & 15;
+      const uint8_t* krow = ring0 + d * SLOT + kt * RBYTES;
+      const int sw = key_swz<NCH>(kt);
+      constexpr int CPS = F::SLICE / 16;
+      uint32_t ad[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) ad[ks] = lds_addr(krow + (((CPS * ks + g) ^ sw) * 16));
+      u32x4 ch[KS];
+      lds_read_chunks<KS>(ad, ch);
+      typename T::Frag b[KS];
+      int sb[KS];
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) {
+        b[ks] = __builtin_bit_cast(bf16x8, ch[ks]);
+        sb[ks] = 127;
+      }
+      // the selection kernels' head-sum order (see the kernel)
+      const float s = qt.score(b, sb);
+      const int j = (wave + i * kSampleWaves) * 16 + kt;
+      if (lane < 16 && j < mq) S[j] = s;
+    }
+  }
+  HK_WAIT_VM(0);  // the loads ahead have landed before the wave leaves its stages
+}
+
+// Scaled formats: the operand layout gathered straight into registers, the
+// next kSampleDepth - 1 blocks of the wave in flight while it scores one.
+// (Their rows are half or a quarter of bf16's, and the staged form measured
+// slower for them: its LDS halves the waves per CU.)  Blocks past the last
+// one fetch nothing.
+template <int RB4, int D, int FMT>
+__device__ __forceinline__ void sample_scores_direct(const SampleArgs& a, const QueryTile<RB4, D, FMT>& qt,
+                                                     QRange rg, int ctx, int mq, float* S) {
+  using T = QueryTile<RB4, D, FMT>;
+  constexpr int KS = T::KS;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int ncb = (mq + 15) / 16;
+  typename T::Frag buf[kSampleDepth][KS];
+  int sbuf[kSampleDepth][KS];
+  int kpos[kSampleDepth];
+  float ksc[kSampleDepth];
+  auto fetch = [&](int i, int slot) {  // the wave's i-th block into ring slot `slot`
+    const int j = (wave + i * kSampleWaves) * 16 + (lane & 15);
+    const int pos = j < mq ? rg.lo + (int)(((int64_t)j * ctx) / mq) : -1;
+    kpos[slot] = pos;
+    T::key(a.k, a.k_scale, pos, buf[slot], sbuf[slot]);
+    if constexpr (FMT == kFP8) ksc[slot] = pos >= 0 ? static_cast<const float*>(a.k_scale)[pos] : 0.0f;
+  };
+  const int nmine = wave < ncb ? (ncb - wave + kSampleWaves - 1) / kSampleWaves : 0;  // wave-uniform
+#pragma unroll
+  for (int d = 0; d < kSampleDepth - 1; ++d) fetch(d, d);
+  for (int i0 = 0; i0 < nmine; i0 += kSampleDepth) {
+#pragma unroll
+    for (int d = 0; d < kSampleDepth; ++d) {
+      const int i = i0 + d;
+      if (i >= nmine) break;  // wave-uniform
+      fetch(i + kSampleDepth - 1, (d + kSampleDepth - 1) % kSampleDepth);
+      float s = qt.score(buf[d], sbuf[d]);
+      if constexpr (FMT == kFP8) s *= ksc[d];
+      const int j = (wave + i * kSampleWaves) * 16 + (lane & 15);
+      if (lane < 16 && kpos[d] >= 0) S[j] = s;
+    }
+  }
+}
 
 // One query per workgroup.  Row block rb of the A operand holds heads
 // 16 rb .. 16 rb + 15 of the query; output lane group g holds heads
-// 16 rb + 4 g + i, summed in-lane, then across the four lane groups.
+// 16 rb + 4 g + i, summed in-lane, then across the four lane groups.  Every
+// sample's score follows the selection kernels' head-sum order, so it is
+// bit-identical to the score the fused kernel compares with tau and the r
+// sampled keys at or above tau always pass.
 template <int RB4, int D, int FMT>
 __global__ void __launch_bounds__(kSampleThreads) sample_tau_kernel(SampleArgs a) {
   using T = QueryTile<RB4, D, FMT>;
-  using Frag = typename T::Frag;
-  constexpr int KS = T::KS;
   extern __shared__ float S[];  // sample scores, M_q entries
   __shared__ RadixScratch sc;
-  __shared__ __attribute__((aligned(16))) uint32_t lin_lds[kSampleThreads / kWave][kLinWords];
+  __shared__ __attribute__((aligned(16))) uint32_t lin_lds[kSampleWaves][kLinWords];
 
-  const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  const int tid = threadIdx.x, wave = tid >> 6;
   // Workgroups are dispatched to the 8 XCDs round-robin; each XCD takes a
   // contiguous run of queries instead, whose sample positions nearly
   // coincide, so that their key gathers hit that XCD's own L2.
@@ -242,41 +433,10 @@ __global__ void __launch_bounds__(kSampleThreads) sample_tau_kernel(SampleArgs a
 
   T qt;
   qt.load(a.q, a.w, a.q_scale, a.H, q, lin_lds[wave]);
-
-  // Wave w scores column blocks w, w + 4, ... of 16 samples, with the
-  // gathers of the next kSampleDepth - 1 of its blocks in flight while it
-  // scores one (the gathers, served from L2 and beyond, are the latency to
-  // hide).  Blocks past the last one fetch nothing.
-  const int ncb = (mq + 15) / 16;
-  constexpr int kStride = kSampleThreads / kWave;
-  Frag buf[kSampleDepth][KS];
-  int sbuf[kSampleDepth][KS];
-  int kpos[kSampleDepth];
-  float ksc[kSampleDepth];
-  auto fetch = [&](int i, int slot) {  // the wave's i-th block into ring slot `slot`
-    const int j = (wave + i * kStride) * 16 + (lane & 15);
-    const int pos = j < mq ? rg.lo + (int)(((int64_t)j * ctx) / mq) : -1;
-    kpos[slot] = pos;
-    T::key(a.k, a.k_scale, pos, buf[slot], sbuf[slot]);
-    if constexpr (FMT == kFP8) ksc[slot] = pos >= 0 ? static_cast<const float*>(a.k_scale)[pos] : 0.0f;
-  };
-  const int nmine = wave < ncb ? (ncb - wave + kStride - 1) / kStride : 0;  // wave-uniform
-#pragma unroll
-  for (int d = 0; d < kSampleDepth - 1; ++d) fetch(d, d);
-  for (int i0 = 0; i0 < nmine; i0 += kSampleDepth) {
-#pragma unroll
-    for (int d = 0; d < kSampleDepth; ++d) {
-      const int i = i0 + d;
-      if (i >= nmine) break;  // wave-uniform
-      fetch(i + kSampleDepth - 1, (d + kSampleDepth - 1) % kSampleDepth);
-      // The selection kernels' head-sum order: a sampled key's score is
-      // bit-identical to the score the fused kernel compares with tau, so the
-      // r sampled keys at or above tau always pass.
-      float s = qt.score(buf[d], sbuf[d]);
-      if constexpr (FMT == kFP8) s *= ksc[d];
-      const int j = (wave + i * kStride) * 16 + (lane & 15);
-      if (lane < 16 && kpos[d] >= 0) S[j] = s;
-    }
+  if constexpr (FMT == kBF16) {
+    sample_scores_staged<RB4, D>(a, qt, rg, ctx, mq, S);
+  } else {
+    sample_scores_direct<RB4, D, FMT>(a, qt, rg, ctx, mq, S);
   }
   __syncthreads();
   int rem, mult;

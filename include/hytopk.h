@@ -26,7 +26,9 @@
  *
  * Conventions for every entry point
  *   * All array arguments are DEVICE pointers to row-major, contiguous data on
- *     the current HIP device, except `stats`, which is a host pointer.
+ *     the current HIP device, except `stats`, which is a host pointer.  q and
+ *     k must be 16-byte aligned (their rows are read in 16-byte pieces), w,
+ *     q_scale and k_scale 4-byte aligned; otherwise HYTOPK_EINVAL.
  *   * q is [n][H][d], k is [L][d], in one of four storage formats (dtype):
  *       HYTOPK_BF16        bf16; q_scale = k_scale = NULL;
  *       HYTOPK_FP8_E4M3    OCP FP8 E4M3 bytes with fp32 per-token

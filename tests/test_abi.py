@@ -94,6 +94,16 @@ def test_null_pointers_and_workspace_errors(lib):
     p8 = _prob(dtype=hk.FP8_E4M3)
     assert lib.hytopk_replay(ctypes.byref(p8), fake, None, fake, None, fake, fake, fake, None) == -1
     assert lib.hytopk_status_string(-3).decode() == "bad workspace"
+    # misaligned inputs -> -1, before any HIP call: q and k 16-byte aligned,
+    # w and the scale arrays 4-byte aligned
+    odd16, odd4 = ctypes.c_void_p(0x1008), ctypes.c_void_p(0x1002)
+    assert lib.hytopk_select(ctypes.byref(p), None, odd16, None, fake, None, fake, fake, None,
+                             fake, 1 << 40, None, None) == -1
+    assert lib.hytopk_replay(ctypes.byref(p), fake, None, odd16, None, fake, fake, fake, None) == -1
+    assert lib.hytopk_replay(ctypes.byref(p), fake, None, fake, None, odd4, fake, fake, None) == -1
+    pmx = _prob(dtype=hk.MXFP8_E4M3)
+    assert lib.hytopk_replay(ctypes.byref(pmx), fake, fake, fake, odd4, fake, fake, fake, None) == -1
+    assert "aligned" in lib.hytopk_last_error().decode()
 
 
 def test_bad_params_are_rejected(lib):
