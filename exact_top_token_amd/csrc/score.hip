@@ -14,6 +14,8 @@
 //     explainer's contest paragraph; also the recovery and full-rescore path).
 // Both modes share the scoring code, so a query's scores are bit-identical on
 // every path.
+#include <type_traits>
+
 #include "launch.h"
 #include "tile.h"
 
@@ -159,6 +161,10 @@ score_tile_kernel(ScoreArgs a) {
   float tau = 0.0f;
   if (!ROWS) tau = qs >= 0 ? a.tau[qs] : 0.0f;
   const bool owner = (lane & 16) == 0;  // lanes 0..15 and 32..47 own distinct (query, key)
+  // Keys [in_lo, in_hi) lie inside both queries' ranges (wave-uniform; empty
+  // when a query is absent).
+  const int in_lo = max(ra.lo, rb.lo);
+  const int in_hi = (qa >= 0 && qb >= 0) ? min(min(ra.hi, rb.hi) + 1, ke) : 0;
 
   int cntA = 0, cntB = 0;  // candidates staged (OWN: emitted) per query (wave-uniform)
 
@@ -212,18 +218,22 @@ score_tile_kernel(ScoreArgs a) {
       }
     } else {
       // One uniform branch per pass: the candidate path runs only when some
-      // key of the 64 passes (about one pass in two at the 1M shape).
-      bool any = false;
+      // key of the 64 passes (about one pass in two at the 1M shape).  A
+      // pass inside both queries' key ranges (all but the edges) skips the
+      // per-key range test: IN is a compile-time copy of that uniform fact.
+      auto candidates = [&](auto in_c) {
+        constexpr bool IN = decltype(in_c)::value;
+        auto passes = [&](int cb, int key) {
+          return owner && (IN || (key >= first && key < lim)) && sc[cb] >= tau;
+        };
+        bool any = false;
 #pragma unroll
-      for (int cb = 0; cb < NCP; ++cb) {
-        const int key = k0 + cb * 16 + (lane & 15);
-        any |= owner && key >= first && key < lim && sc[cb] >= tau;
-      }
-      if (__ballot(any)) {
+        for (int cb = 0; cb < NCP; ++cb) any |= passes(cb, k0 + cb * 16 + (lane & 15));
+        if (!__ballot(any)) return;
 #pragma unroll
         for (int cb = 0; cb < NCP; ++cb) {
           const int key = k0 + cb * 16 + (lane & 15);
-          const bool pass = owner && key >= first && key < lim && sc[cb] >= tau;
+          const bool pass = passes(cb, key);
           const uint64_t m = __ballot(pass);
           if (m) {
             const uint32_t mA = (uint32_t)(m & 0xFFFFull);
@@ -247,6 +257,11 @@ score_tile_kernel(ScoreArgs a) {
             }
           }
         }
+      };
+      if (k0 >= in_lo && k0 + NCP * 16 <= in_hi) {
+        candidates(std::true_type{});
+      } else {
+        candidates(std::false_type{});
       }
     }
   };
