@@ -279,13 +279,27 @@ score_tile_kernel(ScoreArgs a) {
     const int tl = tile_of(it);
     KeyScales ksc;
     if constexpr (F::SCALED) {
+      const int key0 = kb + tl * TK + (lane & 15);
+      if (tl < full_tiles) {  // uniform: one address, the column blocks at fixed offsets
+        const float* pf = static_cast<const float*>(a.k_scale) + key0;
+        const uint8_t* pe = static_cast<const uint8_t*>(a.k_scale) + (int64_t)key0 * T::NBLK + g;
 #pragma unroll
-      for (int cb = 0; cb < NCB; ++cb) {
-        const int key = min(kb + tl * TK + cb * 16 + (lane & 15), a.L - 1);
-        if constexpr (FMT == kFP8) {
-          ksc.f[cb] = static_cast<const float*>(a.k_scale)[key];
-        } else {
-          ksc.e[cb] = static_cast<const uint8_t*>(a.k_scale)[(int64_t)key * T::NBLK + g];
+        for (int cb = 0; cb < NCB; ++cb) {
+          if constexpr (FMT == kFP8) {
+            ksc.f[cb] = pf[cb * 16];
+          } else {
+            ksc.e[cb] = pe[cb * 16 * T::NBLK];
+          }
+        }
+      } else {  // the last tile: keys past L read key L - 1
+#pragma unroll
+        for (int cb = 0; cb < NCB; ++cb) {
+          const int key = min(key0 + cb * 16, a.L - 1);
+          if constexpr (FMT == kFP8) {
+            ksc.f[cb] = static_cast<const float*>(a.k_scale)[key];
+          } else {
+            ksc.e[cb] = static_cast<const uint8_t*>(a.k_scale)[(int64_t)key * T::NBLK + g];
+          }
         }
       }
     }
