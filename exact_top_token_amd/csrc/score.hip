@@ -223,22 +223,29 @@ score_tile_kernel(ScoreArgs a) {
       // per-key range test: IN is a compile-time copy of that uniform fact.
       auto candidates = [&](auto in_c) {
         constexpr bool IN = decltype(in_c)::value;
-        auto passes = [&](int cb, int key) {
-          return owner && (IN || (key >= first && key < lim)) && sc[cb] >= tau;
+        // The ballots are taken of the comparisons themselves (lanes 16..31
+        // and 48..63 hold the same scores as their partners and are masked
+        // out afterwards), so they stay scalar masks with no vector work.
+        constexpr uint64_t kOwners = 0x0000FFFF0000FFFFull;
+        auto hits = [&](int cb, int key) {
+          return (IN || (key >= first && key < lim)) && sc[cb] >= tau;
         };
-        bool any = false;
+        uint64_t mcb[NCP];
+        uint64_t any = 0;
 #pragma unroll
-        for (int cb = 0; cb < NCP; ++cb) any |= passes(cb, k0 + cb * 16 + (lane & 15));
-        if (!__ballot(any)) return;
+        for (int cb = 0; cb < NCP; ++cb) {
+          mcb[cb] = __builtin_amdgcn_ballot_w64(hits(cb, k0 + cb * 16 + (lane & 15))) & kOwners;
+          any |= mcb[cb];
+        }
+        if (!any) return;
 #pragma unroll
         for (int cb = 0; cb < NCP; ++cb) {
           const int key = k0 + cb * 16 + (lane & 15);
-          const bool pass = passes(cb, key);
-          const uint64_t m = __ballot(pass);
+          const uint64_t m = mcb[cb];
           if (m) {
             const uint32_t mA = (uint32_t)(m & 0xFFFFull);
             const uint32_t mB = (uint32_t)((m >> 32) & 0xFFFFull);
-            if (pass) {
+            if (owner && hits(cb, key)) {
               const uint32_t mm = sel ? mB : mA;
               const int rank = __popc(mm & ((1u << (lane & 15)) - 1u));
               const int slot = (sel ? cntB : cntA) + rank;
