@@ -210,41 +210,6 @@ constexpr int kSampleWaves = kSampleThreads / kWave;
 constexpr int kSampleDepth = 3;      // scaled formats: column blocks of gathers in flight per wave
 constexpr int kSampleRing = 8192;    // bf16: bytes of staged key rows per wave
 
-// LDS byte address of a pointer into a __shared__ array.
-__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
-  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
-}
-
-// Reads N 16-byte chunks of a staged block in one asm block that also waits
-// for them.  The compiler does not see these reads, so it does not make
-// them wait for every direct-to-LDS load still in flight (its own analysis
-// cannot tell the ring's stages apart and would, serialising the ring); the
-// wait before them is explicit.  Outputs are early-clobber, and the asm
-// waits for its loads before it ends.
-template <int N>
-__device__ __forceinline__ void lds_read_chunks(const uint32_t (&ad)[N], u32x4 (&r)[N]) {
-  static_assert(N == 2 || N == 4, "two or four chunks");
-  if constexpr (N == 4) {
-    asm volatile(
-        "ds_read_b128 %0, %4\n\t"
-        "ds_read_b128 %1, %5\n\t"
-        "ds_read_b128 %2, %6\n\t"
-        "ds_read_b128 %3, %7\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
-        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
-        : "memory");
-  } else {
-    asm volatile(
-        "ds_read_b128 %0, %2\n\t"
-        "ds_read_b128 %1, %3\n\t"
-        "s_waitcnt lgkmcnt(0)"
-        : "=&v"(r[0]), "=&v"(r[1])
-        : "v"(ad[0]), "v"(ad[1])
-        : "memory");
-  }
-}
-
 // Loads samples j0 .. j0 + 15 of a query (positions P[j], j < mq; rows past
 // the samples load row `lo` and are never scored) into the wave's stage
 // `dst`: OPS direct-to-LDS loads of 1 KB (load p, lane l: key p * KPI + dkk,
@@ -332,23 +297,12 @@ __device__ __forceinline__ void sample_scores_staged(const SampleArgs& a, const 
       const int i = i0 + d;
       issue(i + DEPTH - 1, (d + DEPTH - 1) % DEPTH);
       HK_WAIT_VM((DEPTH - 1) * OPS);  // block i's loads have landed
-      // lane (kt, g): chunk CPS ks + g of key kt, for each k-step
       const int kt = lane & 15;
-      const uint8_t* krow = ring0 + d * SLOT + kt * RBYTES;
-      const int sw = key_swz<NCH>(kt);
-      constexpr int CPS = F::SLICE / 16;
-      uint32_t ad[KS];
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) ad[ks] = lds_addr(krow + (((CPS * ks + g) ^ sw) * 16));
-      u32x4 ch[KS];
-      lds_read_chunks<KS>(ad, ch);
       typename T::Frag b[KS];
       int sb[KS];
+      stage_frags_bf16<D>(ring0 + d * SLOT + kt * RBYTES, kt, g, b);
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        b[ks] = __builtin_bit_cast(bf16x8, ch[ks]);
-        sb[ks] = 127;
-      }
+      for (int ks = 0; ks < KS; ++ks) sb[ks] = 127;
       // the selection kernels' head-sum order (see the kernel)
       const float s = qt.score(b, sb);
       const int j = (wave + i * kSampleWaves) * 16 + kt;

@@ -66,11 +66,19 @@ score_tile_kernel(ScoreArgs a) {
   constexpr int KPB = 1024 / RBYTES;                  // keys per 1 KB DMA block
   constexpr int NCB = TK / 16;                        // 16-key column blocks per tile
   static_assert(TILE_BYTES % (kThreads * 16) == 0, "tile must split evenly over the workgroup");
+  // The scaled formats' key scales travel with their tile: one dword per key
+  // (FP8: its fp32 scale; MX: its four E8M0 block bytes) after the rows,
+  // TK / kWaves keys loaded by each wave, so that no scale is a register
+  // load in flight when a stage is read.
+  constexpr int SC_BYTES = F::SCALED ? TK * 4 : 0;
+  constexpr int SKW = TK / kWaves;                     // scale dwords per wave per tile
+  static_assert(!F::SCALED || (T::NBLK == 4 && SKW <= 64), "one dword of scales per key");
+  constexpr int VMT = OPS + (F::SCALED ? 1 : 0);       // vector-memory operations per tile and wave
 
-  __shared__ __attribute__((aligned(1024))) uint8_t t0[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t t1[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t t2[TILE_BYTES];
-  __shared__ __attribute__((aligned(1024))) uint8_t t3[TILE_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t t0[TILE_BYTES + SC_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t t1[TILE_BYTES + SC_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t t2[TILE_BYTES + SC_BYTES];
+  __shared__ __attribute__((aligned(1024))) uint8_t t3[TILE_BYTES + SC_BYTES];
   __shared__ uint2 stage[(ROWS || OWN) ? 1 : kWaves][2][(ROWS || OWN) ? 1 : kSB];
   // per wave: the pieces of its two queries' linear row blocks (scaled formats)
   __shared__ __attribute__((aligned(16))) uint32_t lin_lds[F::SCALED ? kWaves : 1][2 * kLinWords];
@@ -138,6 +146,12 @@ score_tile_kernel(ScoreArgs a) {
         __builtin_amdgcn_global_load_lds(base + off, HK_LDS(buf + (p * kWaves + wave_u) * 1024), 16, 0, 0);
       }
     }
+    if constexpr (F::SCALED) {
+      if (lane < SKW) {  // the instruction issues in every wave (lanes 0 .. SKW - 1 active)
+        const int key = min(k0 + wave * SKW + lane, a.L - 1);
+        lds_dma4(static_cast<const uint8_t*>(a.k_scale) + (int64_t)key * 4, buf + TILE_BYTES + wave_u * SKW * 4);
+      }
+    }
   };
   // Walk position it scores key tile tile_of(it): ascending, or descending
   // when the caller asks for the reversed walk (a determinism check: the
@@ -185,16 +199,11 @@ score_tile_kernel(ScoreArgs a) {
     __builtin_amdgcn_wave_barrier();
   };
 
-  // Per-key scales of a tile's column blocks: fp32 per token (FP8) or the
-  // E8M0 byte of the lane's block (MX).
-  struct KeyScales {
-    float f[NCB];
-    int e[NCB];
-  };
   constexpr int NCP = NCB > 4 ? 4 : NCB;  // column blocks per scoring pass
-  auto compute_part = [&](int it, int part, const uint8_t* tb, const KeyScales& ksc) {
+  auto compute_part = [&](int it, int part, const uint8_t* stage_base) {
     const int k0 = kb + it * TK + part * NCP * 16;
-    tb += part * NCP * 16 * RBYTES;
+    const uint8_t* tb = stage_base + part * NCP * 16 * RBYTES;
+    const uint8_t* scales = stage_base + TILE_BYTES + part * NCP * 16 * 4;
     float sc[NCP];
 #pragma unroll
     for (int cb = 0; cb < NCP; ++cb) {
@@ -202,12 +211,13 @@ score_tile_kernel(ScoreArgs a) {
       Frag b[KS];
       int sb[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) {
-        sb[ks] = F::MX ? ksc.e[part * NCP + cb] : 127;
-        b[ks] = stage_frag<FMT, D>(tb + kt * RBYTES, kt, g, ks);
-      }
+      for (int ks = 0; ks < KS; ++ks) b[ks] = stage_frag<FMT, D>(tb + kt * RBYTES, kt, g, ks);
+      // the key's staged scale dword (scaled formats)
+      const uint32_t sv = F::SCALED ? *reinterpret_cast<const uint32_t*>(scales + 4 * kt) : 0u;
+#pragma unroll
+      for (int ks = 0; ks < KS; ++ks) sb[ks] = F::MX ? (int)((sv >> (8 * (4 * ks + g))) & 0xFFu) : 127;
       float s = qt.score(b, sb);
-      if constexpr (FMT == kFP8) s *= ksc.f[part * NCP + cb];
+      if constexpr (FMT == kFP8) s *= __uint_as_float(sv);
       sc[cb] = s;
     }
     if constexpr (ROWS) {
@@ -273,53 +283,27 @@ score_tile_kernel(ScoreArgs a) {
     }
   };
 
-  auto compute = [&](int it, const uint8_t* tb, const KeyScales& ksc) {
+  auto compute = [&](int it, const uint8_t* tb) {
 #pragma unroll
-    for (int part = 0; part < NCB / NCP; ++part) compute_part(it, part, tb, ksc);
+    for (int part = 0; part < NCB / NCP; ++part) compute_part(it, part, tb);
   };
 
   // Per tile: wait for this wave's loads of tile `it`, barrier (every wave's
   // loads landed; every wave finished tile it-1), refill tile it-1's stage
-  // with tile it+3, score tile it.  Key scales are read before the refill
-  // so that waiting for them never waits for the refill.
+  // with tile it+3, score tile it (its key scales, for the scaled formats,
+  // came with it).
   auto step = [&](int it, const uint8_t* cur, uint8_t* refill) {
     const int tl = tile_of(it);
-    KeyScales ksc;
-    if constexpr (F::SCALED) {
-      const int key0 = kb + tl * TK + (lane & 15);
-      if (tl < full_tiles) {  // uniform: one address, the column blocks at fixed offsets
-        const float* pf = static_cast<const float*>(a.k_scale) + key0;
-        const uint8_t* pe = static_cast<const uint8_t*>(a.k_scale) + (int64_t)key0 * T::NBLK + g;
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          if constexpr (FMT == kFP8) {
-            ksc.f[cb] = pf[cb * 16];
-          } else {
-            ksc.e[cb] = pe[cb * 16 * T::NBLK];
-          }
-        }
-      } else {  // the last tile: keys past L read key L - 1
-#pragma unroll
-        for (int cb = 0; cb < NCB; ++cb) {
-          const int key = min(key0 + cb * 16, a.L - 1);
-          if constexpr (FMT == kFP8) {
-            ksc.f[cb] = static_cast<const float*>(a.k_scale)[key];
-          } else {
-            ksc.e[cb] = static_cast<const uint8_t*>(a.k_scale)[(int64_t)key * T::NBLK + g];
-          }
-        }
-      }
-    }
     if (it + 2 < ntiles) {
-      HK_WAIT_VM(2 * OPS + (F::SCALED ? NCB : 0));
+      HK_WAIT_VM(2 * VMT);
     } else if (it + 1 < ntiles) {
-      HK_WAIT_VM(OPS + (F::SCALED ? NCB : 0));
+      HK_WAIT_VM(VMT);
     } else {
-      HK_WAIT_VM(F::SCALED ? NCB : 0);
+      HK_WAIT_VM(0);
     }
     __builtin_amdgcn_s_barrier();
     if (it + 3 < ntiles) issue(tile_of(it + 3), refill);
-    compute(tl, cur, ksc);
+    compute(tl, cur);
   };
   for (int it = 0; it < ntiles; it += 4) {
     step(it, t0, t3);

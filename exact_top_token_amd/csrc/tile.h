@@ -273,6 +273,10 @@ __device__ __forceinline__ void wave_lds_sync() {
 __device__ __forceinline__ void lds_dma16(const uint8_t* src, uint8_t* dst) {
   __builtin_amdgcn_global_load_lds(src, HK_LDS(dst), 16, 0, 0);
 }
+// The same with 4 bytes per lane (lane l's dword lands at byte 4 l).
+__device__ __forceinline__ void lds_dma4(const uint8_t* src, uint8_t* dst) {
+  __builtin_amdgcn_global_load_lds(src, HK_LDS(dst), 4, 0, 0);
+}
 
 // XOR swizzle of the 16-byte chunks of staged key row kk (NCH chunks per
 // row), so that B-fragment reads (16 bytes per lane) are free of LDS bank
@@ -295,8 +299,14 @@ __host__ __device__ __forceinline__ constexpr int key_swz(int kk) {
   else return (kk >> 1) & (NCH - 1);
 }
 
+// LDS byte address of a pointer into a __shared__ array.
+__device__ __forceinline__ uint32_t lds_addr(const uint8_t* p) {
+  return (uint32_t)(uintptr_t)(const __attribute__((address_space(3))) uint8_t*)p;
+}
+
 // Lane group g's B fragment, k-step ks, of staged key row kt (at `krow`,
-// swizzled by key_swz): the chunks Fmt::frag names, at their stage slots.
+// swizzled by key_swz): the chunks Fmt::frag names, at their stage slots,
+// read with ordinary LDS loads (the compiler schedules each k-step's wait).
 template <int FMT, int D>
 __device__ __forceinline__ typename Fmt<FMT>::Frag stage_frag(const uint8_t* krow, int kt, int g,
                                                               int ks) {
@@ -314,6 +324,60 @@ __device__ __forceinline__ typename Fmt<FMT>::Frag stage_frag(const uint8_t* kro
     const int c = CPS * ks + g;
     return F::frag(krow + ((c ^ sw) * 16) - 16 * g, g);
   }
+}
+
+
+// Reads N 16-byte chunks from LDS in one asm block that also waits for
+// them.  The compiler does not see these reads, so it does not make them
+// wait for direct-to-LDS loads still in flight -- its own analysis cannot
+// tell a ring's stages apart and made every read wait for all of them --
+// and the kernel waits for a stage's loads explicitly before reading it.
+// Outputs are early-clobber, and the asm waits for its loads before it
+// ends.  (The score kernel reads with ordinary loads: there one asm block
+// per column block measured slower, since each k-step's MFMAs could no
+// longer start on their own fragment.)
+template <int N>
+__device__ __forceinline__ void lds_read_chunks(const uint32_t (&ad)[N], u32x4 (&r)[N]) {
+  static_assert(N == 2 || N == 4, "two or four chunks");
+  if constexpr (N == 4) {
+    asm volatile(
+        "ds_read_b128 %0, %4\n\t"
+        "ds_read_b128 %1, %5\n\t"
+        "ds_read_b128 %2, %6\n\t"
+        "ds_read_b128 %3, %7\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1]), "=&v"(r[2]), "=&v"(r[3])
+        : "v"(ad[0]), "v"(ad[1]), "v"(ad[2]), "v"(ad[3])
+        : "memory");
+  } else {
+    asm volatile(
+        "ds_read_b128 %0, %2\n\t"
+        "ds_read_b128 %1, %3\n\t"
+        "s_waitcnt lgkmcnt(0)"
+        : "=&v"(r[0]), "=&v"(r[1])
+        : "v"(ad[0]), "v"(ad[1])
+        : "memory");
+  }
+}
+
+// bf16 B fragments (every k-step) of staged key row kt (at `krow`, swizzled
+// by key_swz), read with lds_read_chunks: chunk CPS ks + g of the row for
+// k-step ks.
+template <int D>
+__device__ __forceinline__ void stage_frags_bf16(const uint8_t* krow, int kt, int g,
+                                                 bf16x8 (&b)[D / Fmt<kBF16>::KMMA]) {
+  using F = Fmt<kBF16>;
+  constexpr int KS = D / F::KMMA;
+  constexpr int NCH = D * F::BITS / 8 / 16;
+  constexpr int CPS = F::SLICE / 16;  // chunks per k-step slice
+  const int sw = key_swz<NCH>(kt);
+  uint32_t ad[KS];
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) ad[ks] = lds_addr(krow + (((CPS * ks + g) ^ sw) * 16));
+  u32x4 ch[KS];
+  lds_read_chunks<KS>(ad, ch);
+#pragma unroll
+  for (int ks = 0; ks < KS; ++ks) b[ks] = __builtin_bit_cast(bf16x8, ch[ks]);
 }
 
 template <int RB, int D, int FMT>
