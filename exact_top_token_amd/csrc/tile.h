@@ -465,22 +465,33 @@ struct PairTile {
   // lane group 1), and the heads contribute (w/2) * |acc|.  A tile holding
   // one query per MFMA (16 heads per row block) sees the same four partials
   // in its four lane groups.
+  //
+  // The MFMAs run as one phase at raised wave priority, the epilogue after
+  // it at normal priority: of the two waves sharing a SIMD, the one in its
+  // MFMA phase then wins every issue conflict with the other's epilogue, so
+  // the matrix pipe is refilled as soon as it frees (measured on gfx950:
+  // 2.5-5% less score time across the formats; the same order without the
+  // priority change gains nothing).
   __device__ __forceinline__ float score(const Frag (&b)[KS], const int (&sb)[KS]) const {
-    // one row block at a time: its k-steps, then its share of the head sum
-    // (row blocks ascending, so the partials follow the canonical order)
-    float se = 0.0f, so = 0.0f;
-    if constexpr (F::SCALED) {
-      const f32x4 l = F::mma_lin(lin, b[0], f32x4{0.f, 0.f, 0.f, 0.f}, lsa, sb[0]);
-      se = (l[0] + l[1]) + (l[2] + l[3]);
-    }
+    f32x4 l{0.f, 0.f, 0.f, 0.f};
+    f32x4 acc[RB];
+    __builtin_amdgcn_s_setprio(1);
+    if constexpr (F::SCALED) l = F::mma_lin(lin, b[0], l, lsa, sb[0]);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+      acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc = F::mma(a[rb][ks], b[ks], acc, sa[rb][ks], sb[ks]);
+      for (int ks = 0; ks < KS; ++ks) acc[rb] = F::mma(a[rb][ks], b[ks], acc[rb], sa[rb][ks], sb[ks]);
+    }
+    __builtin_amdgcn_s_setprio(0);
+    // head sum, row blocks ascending, so the partials follow the canonical order
+    float se = 0.0f, so = 0.0f;
+    if constexpr (F::SCALED) se = (l[0] + l[1]) + (l[2] + l[3]);
+#pragma unroll
+    for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float r = F::SCALED ? __builtin_fabsf(acc[i]) : __builtin_fmaxf(acc[i], 0.0f);
+        const float r = F::SCALED ? __builtin_fabsf(acc[rb][i]) : __builtin_fmaxf(acc[rb][i], 0.0f);
         if (rb & 1) {
           so = __builtin_fmaf(r, wf[rb][i], so);
         } else {
