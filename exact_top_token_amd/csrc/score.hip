@@ -200,23 +200,42 @@ score_tile_kernel(ScoreArgs a) {
   };
 
   constexpr int NCP = NCB > 4 ? 4 : NCB;  // column blocks per scoring pass
+  // B fragments (and the scaled formats' key-scale dword) of column block j
+  // of a stage
+  struct BlockIn {
+    Frag b[KS];
+    uint32_t sv;
+  };
+  auto read_block = [&](const uint8_t* stage_base, int j, BlockIn& in) {
+    const int kt = j * 16 + (lane & 15);
+#pragma unroll
+    for (int ks = 0; ks < KS; ++ks) in.b[ks] = stage_frag<FMT, D>(stage_base + kt * RBYTES, kt, g, ks);
+    in.sv = F::SCALED ? *reinterpret_cast<const uint32_t*>(stage_base + TILE_BYTES + 4 * kt) : 0u;
+  };
+  BlockIn bin;
+  // One key split per query (and the row path): the next block's fragments
+  // are read between this block's MFMA phase and its epilogue.  With several
+  // splits the staged-candidate path has no registers to spare for it.
+  constexpr bool PF = OWN || ROWS;
   auto compute_part = [&](int it, int part, const uint8_t* stage_base) {
     const int k0 = kb + it * TK + part * NCP * 16;
-    const uint8_t* tb = stage_base + part * NCP * 16 * RBYTES;
-    const uint8_t* scales = stage_base + TILE_BYTES + part * NCP * 16 * 4;
     float sc[NCP];
 #pragma unroll
     for (int cb = 0; cb < NCP; ++cb) {
-      const int kt = cb * 16 + (lane & 15);
-      Frag b[KS];
+      const int j = part * NCP + cb;
+      if constexpr (!PF) read_block(stage_base, j, bin);
       int sb[KS];
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) b[ks] = stage_frag<FMT, D>(tb + kt * RBYTES, kt, g, ks);
-      // the key's staged scale dword (scaled formats)
-      const uint32_t sv = F::SCALED ? *reinterpret_cast<const uint32_t*>(scales + 4 * kt) : 0u;
-#pragma unroll
-      for (int ks = 0; ks < KS; ++ks) sb[ks] = F::MX ? (int)((sv >> (8 * (4 * ks + g))) & 0xFFu) : 127;
-      float s = qt.score(b, sb);
+      for (int ks = 0; ks < KS; ++ks) sb[ks] = F::MX ? (int)((bin.sv >> (8 * (4 * ks + g))) & 0xFFu) : 127;
+      const uint32_t sv = bin.sv;
+      typename T::Acc acc;
+      qt.mma_phase(bin.b, sb, acc);
+      if constexpr (PF) {
+        // the next block's fragments load while this block's epilogue runs
+        if (j + 1 < NCB) read_block(stage_base, j + 1, bin);
+        __builtin_amdgcn_sched_barrier(0);
+      }
+      float s = qt.epilogue(acc);
       if constexpr (FMT == kFP8) s *= __uint_as_float(sv);
       sc[cb] = s;
     }
@@ -284,6 +303,7 @@ score_tile_kernel(ScoreArgs a) {
   };
 
   auto compute = [&](int it, const uint8_t* tb) {
+    if constexpr (PF) read_block(tb, 0, bin);
 #pragma unroll
     for (int part = 0; part < NCB / NCP; ++part) compute_part(it, part, tb);
   };

@@ -453,8 +453,10 @@ struct PairTile {
   }
 
   // Scores of both queries against 16 keys whose B fragments are b[ks] (with
-  // E8M0 scales sb[ks] for MX).  Returns this lane's score: query (lane < 32 ?
-  // A : B), key (lane % 16), before the per-key FP8 scale.
+  // E8M0 scales sb[ks] for MX), in two steps: mma_phase fills the
+  // accumulators, epilogue returns this lane's score: query (lane < 32 ?
+  // A : B), key (lane % 16), before the per-key FP8 scale.  Between the two
+  // the caller may reuse the B-fragment registers (the next block's reads).
   //
   // Canonical head-sum order (every kernel that produces a score follows it):
   // per lane, one partial over the even row blocks and one over the odd row
@@ -472,26 +474,30 @@ struct PairTile {
   // the matrix pipe is refilled as soon as it frees (measured on gfx950:
   // 2.5-5% less score time across the formats; the same order without the
   // priority change gains nothing).
-  __device__ __forceinline__ float score(const Frag (&b)[KS], const int (&sb)[KS]) const {
-    f32x4 l{0.f, 0.f, 0.f, 0.f};
-    f32x4 acc[RB];
+  struct Acc {
+    f32x4 h[RB];
+    f32x4 l;
+  };
+  __device__ __forceinline__ void mma_phase(const Frag (&b)[KS], const int (&sb)[KS], Acc& c) const {
+    c.l = f32x4{0.f, 0.f, 0.f, 0.f};
     __builtin_amdgcn_s_setprio(1);
-    if constexpr (F::SCALED) l = F::mma_lin(lin, b[0], l, lsa, sb[0]);
+    if constexpr (F::SCALED) c.l = F::mma_lin(lin, b[0], c.l, lsa, sb[0]);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
-      acc[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
+      c.h[rb] = f32x4{0.f, 0.f, 0.f, 0.f};
 #pragma unroll
-      for (int ks = 0; ks < KS; ++ks) acc[rb] = F::mma(a[rb][ks], b[ks], acc[rb], sa[rb][ks], sb[ks]);
+      for (int ks = 0; ks < KS; ++ks) c.h[rb] = F::mma(a[rb][ks], b[ks], c.h[rb], sa[rb][ks], sb[ks]);
     }
     __builtin_amdgcn_s_setprio(0);
-    // head sum, row blocks ascending, so the partials follow the canonical order
+  }
+  __device__ __forceinline__ float epilogue(const Acc& c) const {
     float se = 0.0f, so = 0.0f;
-    if constexpr (F::SCALED) se = (l[0] + l[1]) + (l[2] + l[3]);
+    if constexpr (F::SCALED) se = (c.l[0] + c.l[1]) + (c.l[2] + c.l[3]);
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb) {
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        const float r = F::SCALED ? __builtin_fabsf(acc[rb][i]) : __builtin_fmaxf(acc[rb][i], 0.0f);
+        const float r = F::SCALED ? __builtin_fabsf(c.h[rb][i]) : __builtin_fmaxf(c.h[rb][i], 0.0f);
         if (rb & 1) {
           so = __builtin_fmaf(r, wf[rb][i], so);
         } else {
