@@ -167,8 +167,8 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm,
 /* Bytes of the library's static scratch used by hytopk_select_noalloc. */
 #define HYTOPK_NOALLOC_SCRATCH_BYTES (64u << 20)
 
-/* hytopk_select for callers that cannot allocate device memory (code under
- * stream capture, tight serving loops, harnesses that forbid allocation):
+/* hytopk_select for callers that cannot allocate device memory (tight
+ * serving loops, harnesses that forbid allocation):
  * the same arguments and results without the workspace, which is taken from a
  * static device buffer of HYTOPK_NOALLOC_SCRATCH_BYTES owned by the library
  * (one per GPU it runs on, held until the process ends).  The call allocates
@@ -178,7 +178,8 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm,
  * rows_chunk or cap to fit).  Every call on a GPU shares that GPU's buffer
  * and leaves its contents behind: calls that overlap on one GPU (on different
  * streams or threads) race and must be serialised by the caller.  Like
- * hytopk_select it synchronises its stream once. */
+ * hytopk_select it synchronises its stream once (to choose the recovery
+ * path), so neither entry point can be recorded under stream capture. */
 int hytopk_select_noalloc(const hytopk_problem* p, const hytopk_params* prm,
                           const void* q, const void* q_scale, const void* k, const void* k_scale,
                           const float* w, int32_t* out_idx, float* out_score, void* stream,
