@@ -220,6 +220,11 @@ score_tile_kernel(ScoreArgs a) {
   auto compute_part = [&](int it, int part, const uint8_t* stage_base) {
     const int k0 = kb + it * TK + part * NCP * 16;
     float sc[NCP];
+    // PF: each block's partner-lane exchange is issued after the next
+    // block's MFMA phase, so no MFMA phase waits for a shuffle issued just
+    // before it (the pass's last exchange is waited for before the compare).
+    float th[NCP], tp[NCP];
+    uint32_t svs[NCP];
 #pragma unroll
     for (int cb = 0; cb < NCP; ++cb) {
       const int j = part * NCP + cb;
@@ -231,13 +236,26 @@ score_tile_kernel(ScoreArgs a) {
       typename T::Acc acc;
       qt.mma_phase(bin.b, sb, acc);
       if constexpr (PF) {
+        if (cb > 0) tp[cb - 1] = __shfl_xor(th[cb - 1], 16);
         // the next block's fragments load while this block's epilogue runs
         if (j + 1 < NCB) read_block(stage_base, j + 1, bin);
         __builtin_amdgcn_sched_barrier(0);
+        th[cb] = qt.half_sum(acc);
+        svs[cb] = sv;
+      } else {
+        float s = qt.epilogue(acc);
+        if constexpr (FMT == kFP8) s *= __uint_as_float(sv);
+        sc[cb] = s;
       }
-      float s = qt.epilogue(acc);
-      if constexpr (FMT == kFP8) s *= __uint_as_float(sv);
-      sc[cb] = s;
+    }
+    if constexpr (PF) {
+      tp[NCP - 1] = __shfl_xor(th[NCP - 1], 16);
+#pragma unroll
+      for (int cb = 0; cb < NCP; ++cb) {
+        float s = th[cb] + tp[cb];  // the epilogue's sum: own half + partner's half
+        if constexpr (FMT == kFP8) s *= __uint_as_float(svs[cb]);
+        sc[cb] = s;
+      }
     }
     if constexpr (ROWS) {
 #pragma unroll

@@ -457,6 +457,8 @@ struct PairTile {
   // accumulators, epilogue returns this lane's score: query (lane < 32 ?
   // A : B), key (lane % 16), before the per-key FP8 scale.  Between the two
   // the caller may reuse the B-fragment registers (the next block's reads).
+  // half_sum is the epilogue without the partner add, for callers that
+  // exchange the halves later.
   //
   // Canonical head-sum order (every kernel that produces a score follows it):
   // per lane, one partial over the even row blocks and one over the odd row
@@ -490,7 +492,8 @@ struct PairTile {
     }
     __builtin_amdgcn_s_setprio(0);
   }
-  __device__ __forceinline__ float epilogue(const Acc& c) const {
+  // This lane's half of the score (its 32 heads), before the partner add.
+  __device__ __forceinline__ float half_sum(const Acc& c) const {
     float se = 0.0f, so = 0.0f;
     if constexpr (F::SCALED) se = (c.l[0] + c.l[1]) + (c.l[2] + c.l[3]);
 #pragma unroll
@@ -505,17 +508,11 @@ struct PairTile {
         }
       }
     }
-    const float t = se + so;
-    // The partner lane's half: for bf16 through a lane swap (VALU only, so
-    // the next MFMA phase waits on no LDS operation; measured 1% faster), for
-    // the scaled formats, whose VALU is the busier unit, through an LDS
-    // shuffle (the swap measured 1-2% slower there).  Both add the same two
-    // values, so the sum is the same.
-    if constexpr (F::SCALED) {
-      return t + __shfl_xor(t, 16);
-    } else {
-      return add_lane_xor16(t);
-    }
+    return se + so;
+  }
+  __device__ __forceinline__ float epilogue(const Acc& c) const {
+    const float t = half_sum(c);
+    return t + __shfl_xor(t, 16);
   }
 };
 
