@@ -175,10 +175,12 @@ score_tile_kernel(ScoreArgs a) {
   float tau = 0.0f;
   if (!ROWS) tau = qs >= 0 ? a.tau[qs] : 0.0f;
   const bool owner = (lane & 16) == 0;  // lanes 0..15 and 32..47 own distinct (query, key)
-  // Keys [in_lo, in_hi) lie inside both queries' ranges (wave-uniform; empty
-  // when a query is absent).
-  const int in_lo = max(ra.lo, rb.lo);
-  const int in_hi = (qa >= 0 && qb >= 0) ? min(min(ra.hi, rb.hi) + 1, ke) : 0;
+  // Keys [in_lo, in_hi) lie inside both queries' ranges (empty when a query
+  // is absent); read into scalars, so the per-pass test is a uniform branch
+  // (the compiler cannot see that the ranges are wave-uniform).
+  const int in_lo = __builtin_amdgcn_readfirstlane(max(ra.lo, rb.lo));
+  const int in_hi =
+      __builtin_amdgcn_readfirstlane((qa >= 0 && qb >= 0) ? min(min(ra.hi, rb.hi) + 1, ke) : 0);
 
   int cntA = 0, cntB = 0;  // candidates staged (OWN: emitted) per query (wave-uniform)
 
