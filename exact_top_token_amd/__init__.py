@@ -16,6 +16,7 @@ __all__ = [
     "baseline_select", "select_workspace_bytes", "baseline_workspace_bytes", "HytopkError",
     "EXPORTS", "BF16", "FP8_E4M3", "MXFP8_E4M3", "MXFP4_E2M1", "PATH_AUTO", "PATH_ROWS_ALL", "trace_enable", "trace_read",
     "backward", "backward_workspace_bytes", "select_noalloc", "NOALLOC_SCRATCH_BYTES",
+    "select_async", "ASYNC_STATUS_WORDS",
 ]
 
 BF16, FP8_E4M3, MXFP8_E4M3, MXFP4_E2M1 = 0, 1, 2, 3
@@ -25,7 +26,7 @@ EXPORTS = (
     "hytopk_select_workspace", "hytopk_baseline_workspace", "hytopk_select", "hytopk_replay",
     "hytopk_baseline_select", "hytopk_backward_workspace", "hytopk_backward",
     "hytopk_status_string", "hytopk_last_error", "hytopk_trace_enable", "hytopk_trace_read",
-    "hytopk_select_noalloc",
+    "hytopk_select_noalloc", "hytopk_select_async",
 )
 NOALLOC_SCRATCH_BYTES = 64 << 20  # HYTOPK_NOALLOC_SCRATCH_BYTES
 
@@ -93,6 +94,9 @@ def load_library():
     lib.hytopk_select_noalloc.argtypes = [P(Problem), P(Params), vp, vp, vp, vp, vp, vp, vp, vp,
                                           P(Stats)]
     lib.hytopk_select_noalloc.restype = ctypes.c_int
+    lib.hytopk_select_async.argtypes = [P(Problem), P(Params), vp, vp, vp, vp, vp, vp, vp, vp, sz,
+                                        vp, vp]
+    lib.hytopk_select_async.restype = ctypes.c_int
     lib.hytopk_replay.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp, vp, vp]
     lib.hytopk_replay.restype = ctypes.c_int
     lib.hytopk_baseline_select.argtypes = [P(Problem), vp, vp, vp, vp, vp, vp, vp, vp, sz, vp]
@@ -269,6 +273,31 @@ def select_noalloc(q, k, w, topk: int, out, *, q_scale=None, k_scale=None, q_sta
     d = st.as_dict()
     d["failed"] = [failed_buf[i] for i in range(min(st.n_failed, int(prob.n)))]
     return idx, score, d
+
+
+ASYNC_STATUS_WORDS = 8
+
+
+def select_async(q, k, w, topk: int, *, workspace, out, status, q_scale=None, k_scale=None,
+                 q_start=None, params=None, q_pos=None, q_first=None, fmt=None):
+    """hytopk_select_async: select into ``out`` = (idx, score) with the caller's
+    ``workspace`` (select_workspace_bytes) and no host synchronisation, so the
+    call can be recorded in a CUDA/HIP graph.  ``status`` (int32
+    [ASYNC_STATUS_WORDS] on the GPU) receives the device status words:
+    status[0] == 1 means more than max_recover queries failed and their rows
+    are not final.  Returns ``out``."""
+    import torch
+    lib = load_library()
+    prob = _problem(q, k, w, topk, q_start, q_pos, q_first, fmt)
+    prm = _params(params)
+    idx, score = out
+    if status.dtype != torch.int32 or status.numel() < ASYNC_STATUS_WORDS or not status.is_contiguous():
+        raise ValueError("status must be a contiguous int32 tensor of ASYNC_STATUS_WORDS entries")
+    _check(lib.hytopk_select_async(ctypes.byref(prob), ctypes.byref(prm) if prm else None,
+                                   _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w),
+                                   _ptr(idx), _ptr(score), _ptr(workspace), workspace.numel(),
+                                   _stream(q), _ptr(status)))
+    return idx, score
 
 
 def replay(q, k, w, idx, *, q_scale=None, k_scale=None, q_start=None, out=None, fmt=None):

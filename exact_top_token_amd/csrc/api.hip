@@ -291,13 +291,14 @@ int64_t ctx_bound(const hytopk_problem* p, int64_t last) {
 // given, else one workgroup per row.
 int rows_path(const hytopk_problem* p, const hk::ScoreArgs& base, const int* qlist, int q_offset,
               int nq, int64_t maxctx, float* rows, int32_t* out_idx, float* out_score,
-              void* split, hipStream_t s) {
+              void* split, hipStream_t s, hk::RowGate gate = hk::RowGate{nullptr, 0, 0}) {
   hk::ScoreArgs a = base;
   a.rows = rows;
   a.row_stride = p->L;
   a.qlist = qlist;
   a.q_offset = q_offset;
   a.nq = nq;
+  a.gate = gate;
   splits(nq, maxctx, p->dtype, a.nsplit, a.split_len);
   {
     Span sp("score_rows", s);
@@ -320,10 +321,11 @@ int rows_path(const hytopk_problem* p, const hk::ScoreArgs& base, const int* qli
     r.scratch = split;
     r.out_idx = out_idx;
     r.out_score = out_score;
+    r.gate = gate;
     HK_HIP(hk::launch_row_select_split(r, s), "split row top-k launch");
   } else {
     HK_HIP(hk::launch_row_topk(rows, p->L, qlist, q_offset, nq, p->q_pos, p->q_first,
-                               (int)p->q_start, p->k, (int)p->L, out_idx, out_score, s),
+                               (int)p->q_start, p->k, (int)p->L, out_idx, out_score, gate, s),
            "row top-k launch");
   }
   return HYTOPK_OK;
@@ -423,11 +425,19 @@ size_t hytopk_baseline_workspace(const hytopk_problem* p) {
   return (size_t)p->n * (size_t)p->L * 4;
 }
 
-int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void* q,
-                  const void* q_scale, const void* k, const void* k_scale, const float* w,
-                  int32_t* out_idx, float* out_score, void* workspace, size_t workspace_bytes,
-                  void* stream, hytopk_stats* stats) {
-  g_err.clear();
+}  // extern "C"
+
+namespace {
+
+// The selection.  status == null: the recovery path is chosen on the host
+// after one synchronisation (hytopk_select).  status != null: nothing
+// synchronises; recovery passes for up to max_recover failures are enqueued
+// with device-side row counts, and the device status words tell whether the
+// failures exceeded max_recover (hytopk_select_async).
+int select_impl(const hytopk_problem* p, const hytopk_params* prm, const void* q,
+                const void* q_scale, const void* k, const void* k_scale, const float* w,
+                int32_t* out_idx, float* out_score, void* workspace, size_t workspace_bytes,
+                void* stream, hytopk_stats* stats, int32_t* status) {
   int rc = check_problem(p);
   if (rc) return rc;
   Params r = resolve(p, prm);
@@ -451,10 +461,13 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
   const int64_t maxctx = ctx_bound(p, p->n);
   const hk::ScoreArgs base = score_args(p, q, q_scale, k, k_scale, w);
 
+  const bool async = status != nullptr;
   hk::DevStats hs{};
   int path = 0;
-  if (r.force_path != HYTOPK_PATH_ROWS_ALL) {
+  if (r.force_path != HYTOPK_PATH_ROWS_ALL || async) {
     HK_HIP(hk::launch_zero(cnt, n, dst, s), "zero launch");
+  }
+  if (r.force_path != HYTOPK_PATH_ROWS_ALL) {
     hk::SampleArgs sa{};
     sa.q = base.q; sa.k = base.k; sa.w = w; sa.q_scale = q_scale; sa.k_scale = k_scale;
     sa.tau = tau; sa.L = (int)p->L; sa.q_start = (int)p->q_start; sa.n = n; sa.H = p->H;
@@ -482,14 +495,34 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
                               r.cap, dst, failed, s),
              "check launch");
     }
-    HK_HIP(hipMemcpyAsync(&hs, dst, sizeof(hs), hipMemcpyDeviceToHost, s), "stats copy");
-    HK_HIP(hipStreamSynchronize(s), "stream sync");
-    path = hs.n_failed > r.max_recover ? 1 : 0;
+    if (async) {
+      path = 3;
+    } else {
+      HK_HIP(hipMemcpyAsync(&hs, dst, sizeof(hs), hipMemcpyDeviceToHost, s), "stats copy");
+      HK_HIP(hipStreamSynchronize(s), "stream sync");
+      path = hs.n_failed > r.max_recover ? 1 : 0;
+    }
   } else {
     path = 2;
   }
 
-  if (path == 0) {
+  if (path == 3) {
+    // No synchronisation: the candidate select skips the failed queries by
+    // itself, and each recovery pass reads the failure count on the device.
+    {
+      Span sp("cand_select", s);
+      HK_HIP(hk::launch_cand_select(cnt, cand, n, p->q_pos, p->q_first, (int)p->q_start, p->k,
+                                    r.cap, (int)p->L, out_idx, out_score, s),
+             "candidate select launch");
+    }
+    const int most = std::min(r.max_recover, n);
+    for (int f0 = 0; f0 < most; f0 += l.rows_n) {
+      const int nf = std::min(l.rows_n, most - f0);
+      rc = rows_path(p, base, failed + f0, 0, nf, maxctx, rows, out_idx, out_score, split, s,
+                     hk::RowGate{&dst->n_failed, r.max_recover, f0});
+      if (rc) return rc;
+    }
+  } else if (path == 0) {
     {
       Span sp("cand_select", s);
       HK_HIP(hk::launch_cand_select(cnt, cand, n, p->q_pos, p->q_first, (int)p->q_start, p->k,
@@ -528,7 +561,32 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void*
     stats->cand_max = hs.cand_max;
     stats->path = path;
   }
+  if (async) HK_HIP(hk::launch_async_status(dst, r.max_recover, status, s), "status launch");
   return HYTOPK_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int hytopk_select(const hytopk_problem* p, const hytopk_params* prm, const void* q,
+                  const void* q_scale, const void* k, const void* k_scale, const float* w,
+                  int32_t* out_idx, float* out_score, void* workspace, size_t workspace_bytes,
+                  void* stream, hytopk_stats* stats) {
+  g_err.clear();
+  return select_impl(p, prm, q, q_scale, k, k_scale, w, out_idx, out_score, workspace,
+                     workspace_bytes, stream, stats, nullptr);
+}
+
+int hytopk_select_async(const hytopk_problem* p, const hytopk_params* prm, const void* q,
+                        const void* q_scale, const void* k, const void* k_scale, const float* w,
+                        int32_t* out_idx, float* out_score, void* workspace,
+                        size_t workspace_bytes, void* stream, int32_t* status) {
+  g_err.clear();
+  if (!status) return fail(HYTOPK_EINVAL, "status is NULL");
+  if (reinterpret_cast<uintptr_t>(status) % 4) return fail(HYTOPK_EINVAL, "status must be 4-byte aligned");
+  return select_impl(p, prm, q, q_scale, k, k_scale, w, out_idx, out_score, workspace,
+                     workspace_bytes, stream, nullptr, status);
 }
 
 int hytopk_select_noalloc(const hytopk_problem* p, const hytopk_params* prm, const void* q,

@@ -333,8 +333,8 @@ template <int D, bool WITH_U, bool TOK>
 static hipError_t bwd_query_d(const BwdArgs& a, hipStream_t s) {
   const int ntile = (a.topk + kBwdTK - 1) / kBwdTK;
   const size_t dyn = (size_t)(((ntile + 1) & ~1) + kBwdDepth) * kBwdTK * (TOK ? 12 : 8);
-  hipError_t e = hipFuncSetAttribute((const void*)bwd_query_kernel<D, WITH_U, TOK>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+  static LdsLimit lim;
+  hipError_t e = raise_dynamic_lds((const void*)bwd_query_kernel<D, WITH_U, TOK>, (int)dyn, lim);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL((bwd_query_kernel<D, WITH_U, TOK>), dim3((unsigned)a.nq), dim3(kBwdThreads),
                      dyn, s, a);

@@ -403,8 +403,8 @@ template <int RB4, int D, int FMT>
 static hipError_t sample_rb(const SampleArgs& a, hipStream_t s) {
   const int mmax = a.M < a.L ? a.M : a.L;
   const size_t lds = (size_t)mmax * sizeof(float);
-  hipError_t e = hipFuncSetAttribute((const void*)sample_tau_kernel<RB4, D, FMT>,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static LdsLimit lim;
+  hipError_t e = raise_dynamic_lds((const void*)sample_tau_kernel<RB4, D, FMT>, (int)lds, lim);
   if (e != hipSuccess) return e;
   dim3 grid((unsigned)a.n), block(kSampleThreads);
   hipLaunchKernelGGL((sample_tau_kernel<RB4, D, FMT>), grid, block, lds, s, a);

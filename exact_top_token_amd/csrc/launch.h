@@ -6,7 +6,51 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace hk {
+
+// Per-device record of the dynamic-LDS limit a kernel was given.
+struct LdsLimit {
+  static constexpr int kDevices = 64;
+  std::atomic<int> bytes[kDevices];
+};
+
+// Raises `fn`'s dynamic-LDS limit to `bytes` on the current device, once:
+// later launches that fit the limit make no runtime call (so a launch
+// recorded in a stream capture after a first call outside it makes none).
+inline hipError_t raise_dynamic_lds(const void* fn, int bytes, LdsLimit& lim) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  const bool cached = dev >= 0 && dev < LdsLimit::kDevices;
+  if (cached && lim.bytes[dev].load(std::memory_order_acquire) >= bytes) return hipSuccess;
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (e != hipSuccess || !cached) return e;
+  int cur = lim.bytes[dev].load(std::memory_order_relaxed);
+  while (cur < bytes && !lim.bytes[dev].compare_exchange_weak(cur, bytes)) {
+  }
+  return hipSuccess;
+}
+
+// Device-side row count of a row-path pass enqueued without a host
+// synchronisation (recovery in hytopk_select_async): the pass covers list
+// entries base .. base + nq - 1 of a list whose length the device holds in
+// *count; entries at or beyond that length do nothing, and a length above
+// max_count (too many failures for recovery) makes the whole pass empty.
+// count == null: every entry of the pass is live.
+struct RowGate {
+  const int* count;
+  int max_count;
+  int base;
+  __device__ __forceinline__ int live(int nq) const {
+    if (!count) return nq;
+    const int c = *count;
+    if (c > max_count) return 0;
+    const int r = c - base;
+    return r < 0 ? 0 : (r < nq ? r : nq);
+  }
+};
 
 // Fused indexer scoring over causal key ranges.
 //   COMPACT (rows == nullptr): keys with score >= tau[q] go to the candidate
@@ -38,6 +82,7 @@ struct ScoreArgs {
   int nsplit;
   int split_len;
   int reverse;         // 1: walk each launch entry's key tiles from last to first
+  RowGate gate;        // ROWS: device-side count of live entries (count null: all nq)
 };
 
 hipError_t launch_score(const ScoreArgs& a, int d, int fmt, hipStream_t s);
@@ -94,6 +139,13 @@ struct DevStats {
 
 hipError_t launch_zero(int* cnt, int n, DevStats* st, hipStream_t s);
 
+// The device status words of hytopk_select_async (HYTOPK_ASYNC_STATUS_WORDS
+// int32): [0] 1 when more than max_recover queries failed (their rows were
+// not recovered), [1] failures, [2] overflows, [3] under-k queries, [4] the
+// largest candidate count, [5], [6] the candidate total (low, high 32 bits),
+// [7] 0.
+hipError_t launch_async_status(const DevStats* st, int max_recover, int32_t* out, hipStream_t s);
+
 // Check: flags queries whose candidate count is above cap or below
 // min(k, ctx) and appends them to `failed`.
 hipError_t launch_check(const int* cnt, int n, const int* qpos, const int* qfirst, int q_start,
@@ -108,7 +160,7 @@ hipError_t launch_cand_select(const int* cnt, const uint2* cand, int n, const in
 // qlist[e] (or q_offset + e).
 hipError_t launch_row_topk(const float* rows, int64_t row_stride, const int* qlist, int q_offset,
                            int nq, const int* qpos, const int* qfirst, int q_start, int topk, int L,
-                           int* out_idx, float* out_score, hipStream_t s);
+                           int* out_idx, float* out_score, RowGate gate, hipStream_t s);
 
 // Exact top-k of a few long score rows, each row split over `nchunk`
 // workgroups of `chunk_len` entries (recovery and the full rescore): three
@@ -132,6 +184,7 @@ struct RowSelArgs {
   void* scratch;       // row_select_scratch_bytes(nq, nchunk, topk) bytes, 256-byte aligned
   int* out_idx;
   float* out_score;
+  RowGate gate;        // device-side count of live entries (count null: all nq)
 };
 
 hipError_t launch_row_select_split(const RowSelArgs& a, hipStream_t s);

@@ -173,6 +173,23 @@ hipError_t launch_check(const int* cnt, int n, const int* qpos, const int* qfirs
   return hipGetLastError();
 }
 
+__global__ void async_status_kernel(const DevStats* st, int max_recover, int32_t* out) {
+  if (threadIdx.x != 0) return;
+  out[0] = st->n_failed > max_recover ? 1 : 0;
+  out[1] = st->n_failed;
+  out[2] = st->n_overflow;
+  out[3] = st->n_underk;
+  out[4] = st->cand_max;
+  out[5] = (int32_t)(uint32_t)(st->cand_total & 0xFFFFFFFFull);
+  out[6] = (int32_t)(uint32_t)(st->cand_total >> 32);
+  out[7] = 0;
+}
+
+hipError_t launch_async_status(const DevStats* st, int max_recover, int32_t* out, hipStream_t s) {
+  hipLaunchKernelGGL(async_status_kernel, dim3(1), dim3(64), 0, s, st, max_recover, out);
+  return hipGetLastError();
+}
+
 // ----------------------------------------------------------------- output
 
 // Sort the `need` selected (key, pos) pairs by (score desc, pos asc) and write
@@ -366,8 +383,8 @@ hipError_t launch_cand_select(const int* cnt, const uint2* cand, int n, const in
                               const int* qfirst, int q_start, int topk, int cap, int L,
                               int* out_idx, float* out_score, hipStream_t s) {
   const size_t lds = cand_select_lds_bytes(cap, topk);
-  hipError_t e = hipFuncSetAttribute((const void*)cand_select_kernel,
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+  static LdsLimit lim;
+  hipError_t e = raise_dynamic_lds((const void*)cand_select_kernel, (int)lds, lim);
   if (e != hipSuccess) return e;
   hipLaunchKernelGGL(cand_select_kernel, dim3((unsigned)n), dim3(kSelThreads), lds, s, cnt, cand,
                      qpos, qfirst, q_start, topk, cap, L, out_idx, out_score);
@@ -387,11 +404,13 @@ struct RowShared {
 
 __global__ void __launch_bounds__(kSelThreads) row_topk_kernel(const float* rows, int64_t row_stride,
                                                                const int* qlist, int q_offset,
-                                                               const int* qpos, const int* qfirst,
-                                                               int q_start, int topk, int L,
-                                                               int* out_idx, float* out_score) {
+                                                               int nq, const int* qpos,
+                                                               const int* qfirst, int q_start,
+                                                               int topk, int L, int* out_idx,
+                                                               float* out_score, RowGate gate) {
   __shared__ RowShared sh;
   const int e = blockIdx.x, tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
+  if (e >= gate.live(nq)) return;  // uniform: not a live entry of this pass
   const int q = qlist ? qlist[e] : q_offset + e;
   const QRange rg = query_range(qpos, qfirst, q_start, L, q);
   const int ctx = max(0, rg.hi - rg.lo + 1);
@@ -456,11 +475,11 @@ __global__ void __launch_bounds__(kSelThreads) row_topk_kernel(const float* rows
 
 hipError_t launch_row_topk(const float* rows, int64_t row_stride, const int* qlist, int q_offset,
                            int nq, const int* qpos, const int* qfirst, int q_start, int topk, int L,
-                           int* out_idx, float* out_score, hipStream_t s) {
+                           int* out_idx, float* out_score, RowGate gate, hipStream_t s) {
   if (nq <= 0) return hipSuccess;
   hipLaunchKernelGGL(row_topk_kernel, dim3((unsigned)nq), dim3(kSelThreads), 0, s, rows,
-                     row_stride, qlist, q_offset, qpos, qfirst, q_start, topk, L, out_idx,
-                     out_score);
+                     row_stride, qlist, q_offset, nq, qpos, qfirst, q_start, topk, L, out_idx,
+                     out_score, gate);
   return hipGetLastError();
 }
 
@@ -551,6 +570,7 @@ __global__ void __launch_bounds__(kSplitThreads) split_hist_kernel(RowSelArgs a,
   using P = SplitPass<PASS>;
   __shared__ int lh[P::BINS];
   const int c = blockIdx.x, e = blockIdx.y, tid = threadIdx.x;
+  if (e >= a.gate.live(a.nq)) return;  // uniform: not a live row of this pass
   const QRange rg = query_range(a.qpos, a.qfirst, a.q_start, a.L, split_query(a, e));
   const int ctx = max(0, rg.hi - rg.lo + 1);
   for (int b = tid; b < P::BINS; b += kSplitThreads) lh[b] = 0;
@@ -605,6 +625,7 @@ __global__ void __launch_bounds__(kSplitThreads) split_pick_kernel(RowSelArgs a,
   constexpr int BPT = P::BINS / kSplitThreads;  // bins per thread
   __shared__ int wsum[kSplitThreads / kWave];
   const int e = blockIdx.x, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (e >= a.gate.live(a.nq)) return;  // uniform: not a live row of this pass
   int r, need;
   uint32_t prefix = 0u, pmask = 0u;
   if constexpr (PASS == 0) {
@@ -672,6 +693,7 @@ __global__ void __launch_bounds__(kSplitThreads) split_emit_kernel(RowSelArgs a,
                                                                    uint2* staging) {
   __shared__ int wcnt[kSplitThreads / kWave];
   const int c = blockIdx.x, e = blockIdx.y, tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (e >= a.gate.live(a.nq)) return;  // uniform: not a live row of this pass
   const int need = st[e].need;
   if (need == 0) return;  // uniform
   const uint32_t v = st[e].prefix;
@@ -747,6 +769,7 @@ __global__ void __launch_bounds__(kSelThreads) split_sort_kernel(RowSelArgs a, c
   __shared__ uint32_t sk[2][kMaxRounds * kSelThreads];
   __shared__ uint32_t sp[2][kMaxRounds * kSelThreads];
   const int e = blockIdx.x, tid = threadIdx.x;
+  if (e >= a.gate.live(a.nq)) return;  // uniform: not a live row of this pass
   const int q = split_query(a, e);
   const int need = st[e].need;
   const uint2* src = staging + (int64_t)e * a.topk;

@@ -89,8 +89,10 @@ score_tile_kernel(ScoreArgs a) {
   auto swz = [](int kk) { return key_swz<NCH>(kk); };
   const int group = blockIdx.x / a.nsplit, split = blockIdx.x % a.nsplit;
   const int e0 = group * kGroupQ + wave * 2;
-  const int ea = e0 < a.nq ? e0 : -1;
-  const int eb = e0 + 1 < a.nq ? e0 + 1 : -1;
+  // live launch entries (ROWS: a recovery pass may hold fewer than nq)
+  const int nq = ROWS ? a.gate.live(a.nq) : a.nq;
+  const int ea = e0 < nq ? e0 : -1;
+  const int eb = e0 + 1 < nq ? e0 + 1 : -1;
   const int qa = ea < 0 ? -1 : (a.qlist ? a.qlist[ea] : a.q_offset + ea);
   const int qb = eb < 0 ? -1 : (a.qlist ? a.qlist[eb] : a.q_offset + eb);
 

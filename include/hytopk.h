@@ -179,11 +179,43 @@ int hytopk_select(const hytopk_problem* p, const hytopk_params* prm,
  * and leaves its contents behind: calls that overlap on one GPU (on different
  * streams or threads) race and must be serialised by the caller.  Like
  * hytopk_select it synchronises its stream once (to choose the recovery
- * path), so neither entry point can be recorded under stream capture. */
+ * path), so neither entry point can be recorded under stream capture
+ * (hytopk_select_async can). */
 int hytopk_select_noalloc(const hytopk_problem* p, const hytopk_params* prm,
                           const void* q, const void* q_scale, const void* k, const void* k_scale,
                           const float* w, int32_t* out_idx, float* out_score, void* stream,
                           hytopk_stats* stats);
+
+/* Words of the device status array of hytopk_select_async. */
+#define HYTOPK_ASYNC_STATUS_WORDS 8
+
+/* hytopk_select without a host synchronisation, for callers that record the
+ * selection in a stream capture (HIP graph) or must not block: the same
+ * arguments, workspace included, and the same results, except when more than
+ * max_recover queries fail the check (see status[0]).  The threshold, the
+ * fused scoring, the check and the candidate select run as in hytopk_select;
+ * the recovery of up to max_recover failed queries (HyScale explainer, HyTopK
+ * paragraph: the few failed queries are rescored over their whole context)
+ * runs as passes enqueued blind, whose kernels read the failure count on the
+ * device and do nothing beyond it.  The full rescore, whose length the host
+ * cannot know without synchronising, is not enqueued.
+ * status: device array of HYTOPK_ASYNC_STATUS_WORDS int32 (4-byte aligned),
+ * written on the stream:
+ *   [0] 1 when more than max_recover queries failed: the output rows of the
+ *       failed queries are then not final (recompute them, e.g. with
+ *       hytopk_select); 0 when every output row is the exact top-k,
+ *   [1] queries that failed the check, [2] of them with more than cap
+ *       candidates, [3] with fewer than min(k, ctx),
+ *   [4] the largest candidate count of a query,
+ *   [5], [6] the candidate total (low, high 32 bits), [7] 0.
+ * With force_path = HYTOPK_PATH_ROWS_ALL every query takes the row path as
+ * in hytopk_select (no check runs; status reads 0).  Every device operation
+ * of the call is a kernel launch (no memset, copy or synchronisation); keep
+ * kernel tracing off while capturing. */
+int hytopk_select_async(const hytopk_problem* p, const hytopk_params* prm,
+                        const void* q, const void* q_scale, const void* k, const void* k_scale,
+                        const float* w, int32_t* out_idx, float* out_score,
+                        void* workspace, size_t workspace_bytes, void* stream, int32_t* status);
 
 /* Selection replay: out_score[i][j] = I(q_start + i, idx[i][j]) for the saved
  * indices idx [n][k] int32 (HyScale explainer, selection-replay paragraph).

@@ -153,6 +153,12 @@ int main() {
   // the allocation-free entry point refuses problems beyond its static scratch
   expect(hytopk_select_noalloc(&p, nullptr, fake, nullptr, fake, nullptr, fw, fi, ff, nullptr, nullptr) ==
              HYTOPK_EWORKSPACE, "noalloc beyond the static scratch");
+  // the asynchronous select: status array required, workspace checked first
+  int32_t* fst = static_cast<int32_t*>(fake);
+  expect(hytopk_select_async(&p, nullptr, fake, nullptr, fake, nullptr, fw, fi, ff, fake, ~size_t(0),
+                             nullptr, nullptr) == HYTOPK_EINVAL, "async without status");
+  expect(hytopk_select_async(&p, nullptr, fake, nullptr, fake, nullptr, fw, fi, ff, fake, 16, nullptr,
+                             fst) == HYTOPK_EWORKSPACE, "async workspace too small");
   // status strings
   for (int s = -5; s <= 0; ++s) expect(hytopk_status_string(s) != nullptr, "status string");
   // tracing toggles without a device

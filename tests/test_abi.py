@@ -104,6 +104,14 @@ def test_null_pointers_and_workspace_errors(lib):
     pmx = _prob(dtype=hk.MXFP8_E4M3)
     assert lib.hytopk_replay(ctypes.byref(pmx), fake, fake, fake, odd4, fake, fake, fake, None) == -1
     assert "aligned" in lib.hytopk_last_error().decode()
+    # the asynchronous select needs a 4-byte aligned device status array
+    assert lib.hytopk_select_async(ctypes.byref(p), None, fake, None, fake, None, fake, fake, None,
+                                   fake, 1 << 40, None, None) == -1
+    assert "status" in lib.hytopk_last_error().decode()
+    assert lib.hytopk_select_async(ctypes.byref(p), None, fake, None, fake, None, fake, fake, None,
+                                   fake, 1 << 40, None, odd4) == -1
+    assert lib.hytopk_select_async(ctypes.byref(p), None, fake, None, fake, None, fake, fake, None,
+                                   fake, 16, None, fake) == -3
 
 
 def test_bad_params_are_rejected(lib):
