@@ -73,15 +73,17 @@ def test_async_equals_select_on_every_recoverable_path(hk, tiny):
         assert status[7] == 0
 
 
-def test_async_reports_unrecovered_failures(hk, tiny):
-    """More failures than max_recover: status[0] is 1, the passing queries'
-    rows are the exact ones, and nothing is written past the recovered rows."""
+@pytest.mark.parametrize("max_recover", [4, 1])
+def test_async_reports_unrecovered_failures(hk, tiny, max_recover):
+    """More failures than max_recover (4 rows in two passes, or 1 row):
+    status[0] is 1, the passing queries' rows are the exact ones, and the
+    failed queries' rows are left untouched."""
     d, inp, cnts = tiny["dev"], tiny["inp"], tiny["cnts"]
     cap_few = int(np.sort(cnts)[-10])
-    prm = dict(cap=cap_few, max_recover=4, rows_chunk=3)
+    prm = dict(cap=cap_few, max_recover=max_recover, rows_chunk=3)
     say(f"async: failures beyond max_recover, params {prm}")
     ref_idx, ref_sc, st = hk.select(d["q"], d["k"], d["w"], inp.k, params=prm, with_stats=True)
-    assert st["path"] == 1 and st["n_failed"] > 4
+    assert st["path"] == 1 and st["n_failed"] > max_recover
     idx, sc, status = _run_async(hk, d, inp, prm)
     assert status[0] == 1 and status[1] == st["n_failed"], status
     failed = set(st["failed"])
