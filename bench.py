@@ -184,6 +184,50 @@ def time_select_replay(hk, inp, t: dict, steps: int, warmup: int) -> dict:
                 phases=phases, stats=stats, idx=idx, sc=sc)
 
 
+def time_graph_step(hk, inp, t: dict, steps: int, ref_idx, ref_sc) -> dict:
+    """The same step (select + replay) recorded once in a HIP graph through
+    hytopk_select_async (no host synchronisation), then replayed `steps`
+    times.  The replays' outputs must equal the eager calls' bit for bit."""
+    import torch
+    dev = t["q"].device
+    q, k, w, qs, ks, fk = t["q"], t["k"], t["w"], t["qs"], t["ks"], t["fk"]
+    ws = torch.empty(hk.select_workspace_bytes(q, k, w, inp.k, **fk), dtype=torch.uint8, device=dev)
+    idx = torch.empty((inp.n, inp.k), dtype=torch.int32, device=dev)
+    sc = torch.empty((inp.n, inp.k), dtype=torch.float32, device=dev)
+    rep = torch.empty_like(sc)
+    status = torch.zeros(hk.ASYNC_STATUS_WORDS, dtype=torch.int32, device=dev)
+
+    def step():
+        hk.select_async(q, k, w, inp.k, q_scale=qs, k_scale=ks, workspace=ws, out=(idx, sc),
+                        status=status, **fk)
+        hk.replay(q, k, w, idx, q_scale=qs, k_scale=ks, out=rep, **fk)
+
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        step()  # outside the capture: the library sets its kernels' LDS limits once
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    g = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(g):
+        step()
+    torch.cuda.synchronize()
+    g.replay()
+    torch.cuda.synchronize()
+    a, b = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    a.record()
+    for _ in range(steps):
+        g.replay()
+    b.record()
+    torch.cuda.synchronize()
+    equal = bool(torch.equal(idx, ref_idx) and torch.equal(sc.view(torch.int32), ref_sc.view(torch.int32)))
+    st = status.cpu().tolist()
+    del g, ws, idx, sc, rep, status
+    torch.cuda.empty_cache()
+    return {"ms_per_step": round(a.elapsed_time(b) / steps, 4), "equal_to_eager": equal,
+            "failures": st[1], "incomplete": st[0]}
+
+
 def workload_summary(inp, m: dict) -> dict:
     """Per-workload figures: select and replay times, and the fused score
     kernel against the MFMA peak of the workload's format."""
@@ -220,6 +264,8 @@ def main() -> int:
     ap.add_argument("--no-cpu", action="store_true", help="skip the oracle CPU baseline")
     ap.add_argument("--no-backward", action="store_true",
                     help="skip timing the indexer backward at the replayed entries")
+    ap.add_argument("--no-graph", action="store_true",
+                    help="skip the graph-recorded step (hytopk_select_async + replay)")
     ap.add_argument("--no-extra", action="store_true",
                     help="skip the extra workloads (" + ", ".join(EXTRA_WORKLOADS) + ")")
     ap.add_argument("--cpu-seconds", type=float, default=15.0)
@@ -307,6 +353,13 @@ def main() -> int:
         if not same:
             log("WARNING: baseline result differs from hytopk_select")
 
+    graph = None
+    if not args.no_graph:
+        log(f"graph: select_async + replay recorded once, {args.steps} replays")
+        graph = time_graph_step(hk, inp, t, args.steps, idx, sc)
+        if not graph["equal_to_eager"]:
+            log("WARNING: graph-replayed result differs from hytopk_select")
+
     bwd = None
     if not args.no_backward:
         log("backward at the replayed entries (dq, dw, dk)")
@@ -388,6 +441,7 @@ def main() -> int:
         "baseline_over_select": None if baseline_ms is None else round(baseline_ms / select_ms, 3),
         "phases_ms": summ["phases_ms"],
         "backward": bwd,
+        "graph": graph,
         "stats": stats,
         "extra_workloads": extra or None,
         "roofline": {"bound": "mfma", "kernel": "score_tile_kernel (fused score+compare+compact)",
