@@ -208,25 +208,75 @@ hipError_t launch_replay(const ReplayArgs& a, int d, int fmt, hipStream_t s) {
 constexpr int kSampleThreads = 256;  // 4 waves share one query's samples
 constexpr int kSampleWaves = kSampleThreads / kWave;
 constexpr int kSampleDepth = 3;      // scaled formats: column blocks of gathers in flight per wave
-constexpr int kSampleRing = 8192;    // bf16: bytes of staged key rows per wave
 
-// Loads samples j0 .. j0 + 15 of a query (positions P[j], j < mq; rows past
-// the samples load row `lo` and are never scored) into the wave's stage
-// `dst`: OPS direct-to-LDS loads of 1 KB (load p, lane l: key p * KPI + dkk,
-// byte offset dsw[p] in its row).
-template <int OPS, int KPI, int RBYTES>
-__device__ __forceinline__ void stage_sample_block(const uint8_t* k, const int* P, int j0, int mq,
-                                                   int lo, int dkk, const int (&dsw)[OPS],
-                                                   uint8_t* dst) {
-  // every position first, so that the LDS reads go out together
-  int rowpos[OPS];
-#pragma unroll
-  for (int p = 0; p < OPS; ++p) {
-    const int js = j0 + p * KPI + dkk;
-    rowpos[p] = js < mq ? P[js] : lo;
-  }
+// Loads the key rows at rowpos[p] (load p: rows p * KPI .. p * KPI + KPI - 1
+// of a 16-sample block, lane l taking row p * KPI + dkk at byte offset
+// dsw[p]) into the wave's stage `dst`: OPS direct-to-LDS loads of 1 KB.
+template <int OPS, int RBYTES>
+__device__ __forceinline__ void stage_rows(const uint8_t* k, const int (&rowpos)[OPS],
+                                           const int (&dsw)[OPS], uint8_t* dst) {
 #pragma unroll
   for (int p = 0; p < OPS; ++p) lds_dma16(k + (int64_t)rowpos[p] * RBYTES + dsw[p], dst + p * 1024);
+}
+
+// Block radix select of the r-th largest of the m sample scores held in
+// registers: thread t holds sample t + 256 k in sv[N - K + k], k < K (the
+// slots below N - K are unused).  The same counting as block_select_largest
+// over the same multiset, so the same result.
+template <int N>
+__device__ uint32_t select_largest_regs(const float (&sv)[N], int K, int m, int r, RadixScratch& sc,
+                                        int& rem, int& mult) {
+  const int tid = threadIdx.x;
+  uint32_t prefix = 0u, pmask = 0u;
+  for (int pass = 3; pass >= 0; --pass) {
+    const int shift = 8 * pass;
+    for (int b = tid; b < 256; b += kSampleThreads) sc.hist[b] = 0;
+    __syncthreads();
+    uint32_t run_d = 0u;
+    int run_n = 0;
+#pragma unroll
+    for (int sl = 0; sl < N; ++sl) {
+      const int k = sl - (N - K);
+      const int i = tid + k * kSampleThreads;
+      if (k >= 0 && i < m) {
+        const uint32_t kk = score_key(sv[sl]);
+        if ((kk & pmask) == prefix) {
+          const uint32_t d = (kk >> shift) & 255u;
+          if (run_n > 0 && d != run_d) {
+            atomicAdd(&sc.hist[run_d], run_n);
+            run_n = 0;
+          }
+          run_d = d;
+          ++run_n;
+        }
+      }
+    }
+    if (run_n > 0) atomicAdd(&sc.hist[run_d], run_n);
+    __syncthreads();
+    int h = 0, suf = 0;
+    if (tid < 256) {
+      h = sc.hist[tid];
+      suf = wave_suffix_sum(h);
+      if (lane_id() == 0) sc.wtot[tid >> 6] = suf;
+    }
+    __syncthreads();
+    if (tid < 256) {
+      for (int v = (tid >> 6) + 1; v < 4; ++v) suf += sc.wtot[v];
+      if (suf >= r && suf - h < r) {
+        sc.digit = (uint32_t)tid;
+        sc.rank = r - (suf - h);
+        sc.mult = h;
+      }
+    }
+    __syncthreads();
+    prefix |= sc.digit << shift;
+    pmask |= 255u << shift;
+    r = sc.rank;
+    __syncthreads();
+  }
+  rem = r;
+  mult = sc.mult;
+  return prefix;
 }
 
 // bf16 samples: the sampled key rows reach the waves through LDS.
@@ -235,68 +285,83 @@ __device__ __forceinline__ void stage_sample_block(const uint8_t* k, const int* 
 // straight from memory gives every lane its own 16-byte piece of a
 // different row: four times the address-unit work per byte, which bounded
 // the gathers (the address path stalled on the cache 62% of the time).
-// Wave w scores column blocks w, w + 4, ...; each wave owns a ring of
-// DEPTH stages, kSampleRing bytes, and waits for a stage's loads by count.
-// S[0 .. mq) first receives the sample positions (computed once, not per
-// load), then the scores; a block's entries are touched only by its wave.
-template <int RB4, int D>
+// Each wave owns two stages (the block it scores and the next one's loads)
+// and waits for a stage's loads by count.  The scores stay in registers
+// (sv, N per thread) and the sample positions are carried per lane, so the
+// workgroup's only LDS is the row ring: measured against keeping positions
+// and scores in 32 KB of LDS per workgroup, the threshold takes 1.68 ->
+// 1.35 ms at the 1M shape.
+template <int RB4, int D, int N>
 __device__ __forceinline__ void sample_scores_staged(const SampleArgs& a, const QueryTile<RB4, D, kBF16>& qt,
-                                                     QRange rg, int ctx, int mq, float* S) {
-  using F = Fmt<kBF16>;
+                                                     QRange rg, int ctx, int mq, float (&sv)[N]) {
   using T = QueryTile<RB4, D, kBF16>;
   constexpr int KS = T::KS, RBYTES = T::RBYTES, NCH = RBYTES / 16;
   constexpr int CB_BYTES = 16 * RBYTES;  // a column block's 16 key rows
-  constexpr int DEPTH = kSampleRing / CB_BYTES;
+  constexpr int DEPTH = 2;               // stages per wave: the block scored and the next
   constexpr int OPS = CB_BYTES / 1024;   // 1 KB loads per column block (= its vector-memory ops)
   constexpr int KPI = 1024 / RBYTES;     // key rows per load
   constexpr int SLOT = kSampleWaves * CB_BYTES;
-  static_assert(CB_BYTES % 1024 == 0 && DEPTH >= 2 && DEPTH <= 4, "stage ring shape");
+  static_assert(CB_BYTES % 1024 == 0, "stage ring shape");
   __shared__ __attribute__((aligned(1024))) uint8_t ring_lds[DEPTH * SLOT];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63, g = lane >> 4;
 
-  // positions lo + floor(j * ctx / mq): thread t takes a run of consecutive
-  // j, one division for its first and the remainder carried from there
-  int* P = reinterpret_cast<int*>(S);
-  {
-    const int per = (mq + kSampleThreads - 1) / kSampleThreads;
-    const int j0 = tid * per, j1 = min(mq, j0 + per);
-    if (j0 < j1) {
-      const int dq = ctx / mq, dr = ctx % mq;
-      const int64_t n0 = (int64_t)j0 * ctx;
-      int pos = (int)(n0 / mq), rem = (int)(n0 % mq);
-      for (int j = j0; j < j1; ++j) {
-        P[j] = rg.lo + pos;
-        pos += dq;
-        rem += dr;
-        if (rem >= mq) { rem -= mq; ++pos; }
-      }
-    }
-  }
-  __syncthreads();
-
-  const int ncb = (mq + 15) / 16;
-  const int nmine = wave < ncb ? (ncb - wave + kSampleWaves - 1) / kSampleWaves : 0;  // wave-uniform
+  // Wave w scores blocks 16 k + 4 w + b (b = 0..3) of 16 samples, so that
+  // sample t + 256 k belongs to thread t (lane group b keeps block b's
+  // scores); K rounds of four blocks cover the mq samples.
+  const int K = (mq + kSampleThreads - 1) / kSampleThreads;
   uint8_t* const ring0 = ring_lds + __builtin_amdgcn_readfirstlane(wave) * CB_BYTES;  // stage s: + s * SLOT
   const int dkk = lane / NCH;
   int dsw[OPS];  // the stage's swizzle: load p fetches this chunk of its row
 #pragma unroll
   for (int p = 0; p < OPS; ++p) dsw[p] = 16 * ((lane % NCH) ^ key_swz<NCH>(p * KPI + dkk));
-  auto issue = [&](int i, int slot) {  // the wave's i-th block into ring slot `slot`
-    stage_sample_block<OPS, KPI, RBYTES>(a.k, P, (wave + i * kSampleWaves) * 16, mq, rg.lo, dkk, dsw,
-                                         ring0 + slot * SLOT);
+  // Positions lo + floor(j * ctx / mq) of this lane's rows, carried from
+  // block to block: the next block is 16 samples on, or 208 from the last
+  // block of a round to the first of the next.
+  // Only load 0's row is carried (position and remainder); the rows of
+  // loads 1.. are KPI samples apart and derived from it at each issue.
+  const int q16 = (int)((int64_t)16 * ctx / mq), r16 = (int)((int64_t)16 * ctx % mq);
+  const int q208 = (int)((int64_t)208 * ctx / mq), r208 = (int)((int64_t)208 * ctx % mq);
+  const int qk = (int)((int64_t)KPI * ctx / mq), rk = (int)((int64_t)KPI * ctx % mq);
+  int jb = __builtin_amdgcn_readfirstlane(wave * 64);  // first sample of the next block (uniform)
+  int pos0, rem0;
+  {
+    const int64_t n0 = (int64_t)(jb + dkk) * ctx;
+    pos0 = (int)(n0 / mq);
+    rem0 = (int)(n0 % mq);
+  }
+  int nissued = 0;
+  auto issue = [&](int slot) {  // the wave's next block into ring slot `slot`
+    int rowpos[OPS];
+    int pp = pos0, rr = rem0;
+#pragma unroll
+    for (int p = 0; p < OPS; ++p) {
+      rowpos[p] = rg.lo + (jb + p * KPI + dkk < mq ? pp : 0);  // past the samples: row lo, never scored
+      pp += qk;
+      rr += rk;
+      if (rr >= mq) {
+        rr -= mq;
+        ++pp;
+      }
+    }
+    const bool round_end = (nissued & 3) == 3;
+    jb += round_end ? 208 : 16;
+    pos0 += round_end ? q208 : q16;
+    rem0 += round_end ? r208 : r16;
+    if (rem0 >= mq) {
+      rem0 -= mq;
+      ++pos0;
+    }
+    ++nissued;
+    stage_rows<OPS, RBYTES>(a.k, rowpos, dsw, ring0 + slot * SLOT);
   };
-  // Straight-line body: loads run DEPTH - 1 blocks ahead unconditionally and
-  // the last round is scored whole (blocks past the wave's last one load row
-  // lo and store nothing: their samples lie past mq), so every block waits
-  // with the same count.
+  issue(0);
+  for (int k = 0; k < K; ++k) {
+    float mine = 0.0f;
 #pragma unroll
-  for (int d = 0; d < DEPTH - 1; ++d) issue(d, d);
-  for (int i0 = 0; i0 < nmine; i0 += DEPTH) {
-#pragma unroll
-    for (int d = 0; d < DEPTH; ++d) {
-      const int i = i0 + d;
-      issue(i + DEPTH - 1, (d + DEPTH - 1) % DEPTH);
-      HK_WAIT_VM((DEPTH - 1) * OPS);  // block i's loads have landed
+    for (int bq = 0; bq < 4; ++bq) {
+      const int d = bq & 1;  // ring slot of this block (blocks alternate)
+      issue(d ^ 1);          // the next block (past the last one: row lo, unscored)
+      HK_WAIT_VM(OPS);       // this block's loads have landed
       const int kt = lane & 15;
       typename T::Frag b[KS];
       int sb[KS];
@@ -305,11 +370,14 @@ __device__ __forceinline__ void sample_scores_staged(const SampleArgs& a, const 
       for (int ks = 0; ks < KS; ++ks) sb[ks] = 127;
       // the selection kernels' head-sum order (see the kernel)
       const float s = qt.score(b, sb);
-      const int j = (wave + i * kSampleWaves) * 16 + kt;
-      if (lane < 16 && j < mq) S[j] = s;
+      if (g == bq) mine = s;
     }
+    // keep this round's score: the slots shift down by one per round
+#pragma unroll
+    for (int sl = 0; sl < N - 1; ++sl) sv[sl] = sv[sl + 1];
+    sv[N - 1] = mine;
   }
-  HK_WAIT_VM(0);  // the loads ahead have landed before the wave leaves its stages
+  HK_WAIT_VM(0);  // the load ahead has landed before the wave leaves its stages
 }
 
 // Scaled formats: the operand layout gathered straight into registers, the
@@ -358,8 +426,11 @@ __device__ __forceinline__ void sample_scores_direct(const SampleArgs& a, const 
 // sample's score follows the selection kernels' head-sum order, so it is
 // bit-identical to the score the fused kernel compares with tau and the r
 // sampled keys at or above tau always pass.
-template <int RB4, int D, int FMT>
-__global__ void __launch_bounds__(kSampleThreads) sample_tau_kernel(SampleArgs a) {
+template <int RB4, int D, int FMT, int N>
+// (Three waves per SIMD: the bf16 path fits 168 registers with its 32 sample
+// scores per thread, and its row ring leaves the LDS for three workgroups.)
+__global__ void __launch_bounds__(kSampleThreads) __attribute__((amdgpu_waves_per_eu(3)))
+sample_tau_kernel(SampleArgs a) {
   using T = QueryTile<RB4, D, FMT>;
   extern __shared__ float S[];  // sample scores, M_q entries
   __shared__ RadixScratch sc;
@@ -387,28 +458,47 @@ __global__ void __launch_bounds__(kSampleThreads) sample_tau_kernel(SampleArgs a
 
   T qt;
   qt.load(a.q, a.w, a.q_scale, a.H, q, lin_lds[wave]);
+  int rem, mult;
+  uint32_t v;
   if constexpr (FMT == kBF16) {
-    sample_scores_staged<RB4, D>(a, qt, rg, ctx, mq, S);
+    // bf16: the sample scores stay in registers (N per thread), so the
+    // workgroup's LDS is only its row ring
+    float sv[N];
+#pragma unroll
+    for (int i = 0; i < N; ++i) sv[i] = 0.0f;
+    sample_scores_staged<RB4, D, N>(a, qt, rg, ctx, mq, sv);
+    __syncthreads();
+    v = select_largest_regs<N>(sv, (mq + kSampleThreads - 1) / kSampleThreads, mq, r, sc, rem, mult);
   } else {
     sample_scores_direct<RB4, D, FMT>(a, qt, rg, ctx, mq, S);
+    __syncthreads();
+    v = block_select_largest(
+        mq, r, [&](int i) { return score_key(S[i]); }, [](int) { return true; }, sc, rem, mult);
   }
-  __syncthreads();
-  int rem, mult;
-  const uint32_t v = block_select_largest(
-      mq, r, [&](int i) { return score_key(S[i]); }, [](int) { return true; }, sc, rem, mult);
   if (tid == 0) a.tau[q] = key_score(v);
+}
+
+template <int RB4, int D, int FMT, int N>
+static hipError_t sample_launch(const SampleArgs& a, size_t lds, hipStream_t s) {
+  static LdsLimit lim;
+  if (lds) {
+    hipError_t e = raise_dynamic_lds((const void*)sample_tau_kernel<RB4, D, FMT, N>, (int)lds, lim);
+    if (e != hipSuccess) return e;
+  }
+  dim3 grid((unsigned)a.n), block(kSampleThreads);
+  hipLaunchKernelGGL((sample_tau_kernel<RB4, D, FMT, N>), grid, block, lds, s, a);
+  return hipGetLastError();
 }
 
 template <int RB4, int D, int FMT>
 static hipError_t sample_rb(const SampleArgs& a, hipStream_t s) {
   const int mmax = a.M < a.L ? a.M : a.L;
-  const size_t lds = (size_t)mmax * sizeof(float);
-  static LdsLimit lim;
-  hipError_t e = raise_dynamic_lds((const void*)sample_tau_kernel<RB4, D, FMT>, (int)lds, lim);
-  if (e != hipSuccess) return e;
-  dim3 grid((unsigned)a.n), block(kSampleThreads);
-  hipLaunchKernelGGL((sample_tau_kernel<RB4, D, FMT>), grid, block, lds, s, a);
-  return hipGetLastError();
+  if constexpr (FMT == kBF16) {  // scores in registers: 32 or 64 per thread
+    if (mmax <= 32 * kSampleThreads) return sample_launch<RB4, D, FMT, 32>(a, 0, s);
+    return sample_launch<RB4, D, FMT, 64>(a, 0, s);
+  } else {
+    return sample_launch<RB4, D, FMT, 1>(a, (size_t)mmax * sizeof(float), s);
+  }
 }
 
 template <int FMT>
