@@ -396,9 +396,25 @@ __device__ __forceinline__ void sample_scores_direct(const SampleArgs& a, const 
   int sbuf[kSampleDepth][KS];
   int kpos[kSampleDepth];
   float ksc[kSampleDepth];
-  auto fetch = [&](int i, int slot) {  // the wave's i-th block into ring slot `slot`
-    const int j = (wave + i * kSampleWaves) * 16 + (lane & 15);
-    const int pos = j < mq ? rg.lo + (int)(((int64_t)j * ctx) / mq) : -1;
+  // This lane's sample position, carried from block to block (the wave's
+  // blocks are 16 * waves samples apart): no division per fetch.
+  constexpr int STEP = 16 * kSampleWaves;
+  const int sq = (int)((int64_t)STEP * ctx / mq), sr = (int)((int64_t)STEP * ctx % mq);
+  int jc = wave * 16 + (lane & 15), pc, rc;
+  {
+    const int64_t n0 = (int64_t)jc * ctx;
+    pc = (int)(n0 / mq);
+    rc = (int)(n0 % mq);
+  }
+  auto fetch = [&](int i, int slot) {  // the wave's i-th block (fetched in order) into `slot`
+    const int pos = jc < mq ? rg.lo + pc : -1;
+    jc += STEP;
+    pc += sq;
+    rc += sr;
+    if (rc >= mq) {
+      rc -= mq;
+      ++pc;
+    }
     kpos[slot] = pos;
     T::key(a.k, a.k_scale, pos, buf[slot], sbuf[slot]);
     if constexpr (FMT == kFP8) ksc[slot] = pos >= 0 ? static_cast<const float*>(a.k_scale)[pos] : 0.0f;
