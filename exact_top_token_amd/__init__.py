@@ -127,6 +127,50 @@ def _ptr(t):
     return None if t is None else ctypes.c_void_p(t.data_ptr())
 
 
+def _need(t, name: str, shape, dtype, device) -> None:
+    """The library writes or reads these buffers by the problem's sizes, so
+    a caller-given tensor must have exactly that shape and dtype, be
+    contiguous and sit on the inputs' device."""
+    if (tuple(t.shape) != tuple(shape) or t.dtype != dtype or not t.is_contiguous()
+            or t.device != device):
+        raise ValueError(f"{name} must be a contiguous {dtype} tensor of shape {tuple(shape)} "
+                         f"on {device}, got {t.dtype} {tuple(t.shape)} on {t.device}")
+
+
+def _workspace(t, device):
+    """Workspace: contiguous uint8 on the inputs' device (its size is checked by the library)."""
+    import torch
+    if t.dtype != torch.uint8 or t.dim() != 1 or not t.is_contiguous() or t.device != device:
+        raise ValueError(f"workspace must be a contiguous 1-D uint8 tensor on {device}")
+    return t
+
+
+def _scales(prob, q, q_scale, k_scale) -> None:
+    """Per-token fp32 scales (FP8) or E8M0 bytes per 32 elements (MX)."""
+    import torch
+    if prob.dtype == BF16:
+        if q_scale is not None or k_scale is not None:
+            raise ValueError("bf16 inputs take no q_scale / k_scale")
+        return
+    if q_scale is None or k_scale is None:
+        raise ValueError("fp8 and MX inputs need q_scale and k_scale")
+    if prob.dtype == FP8_E4M3:
+        _need(q_scale, "q_scale", (prob.n,), torch.float32, q.device)
+        _need(k_scale, "k_scale", (prob.L,), torch.float32, q.device)
+    else:
+        _need(q_scale, "q_scale", (prob.n, prob.H, prob.d // 32), torch.uint8, q.device)
+        _need(k_scale, "k_scale", (prob.L, prob.d // 32), torch.uint8, q.device)
+
+
+def _outputs(out, prob, device):
+    import torch
+    idx, score = out
+    _need(idx, "out[0] (indices)", (prob.n, prob.k), torch.int32, device)
+    if score is not None:
+        _need(score, "out[1] (scores)", (prob.n, prob.k), torch.float32, device)
+    return idx, score
+
+
 def _dtype_code(q, fmt=None) -> int:
     """Storage format: ``fmt`` ("bf16", "fp8", "mxfp8", "mxfp4") when given,
     else bf16 or per-token FP8 from the tensor dtype."""
@@ -150,11 +194,15 @@ def _problem(q, k, w, topk: int, q_start, q_pos=None, q_first=None, fmt=None) ->
     if k.shape[1] != dq or tuple(w.shape) != (n, H):
         raise ValueError("shapes must be q [n][H][d], k [L][d], w [n][H]")
     for t in (q, k, w):
-        if not t.is_cuda or not t.is_contiguous():
-            raise ValueError("tensors must be contiguous and on the GPU")
+        if not t.is_cuda or not t.is_contiguous() or t.device != q.device:
+            raise ValueError("q, k and w must be contiguous and on the same GPU")
+    if w.dtype != torch.float32:
+        raise ValueError("w must be float32")
+    if k.dtype != q.dtype or (code in (MXFP8_E4M3, MXFP4_E2M1) and q.dtype != torch.uint8):
+        raise ValueError("q and k must share a dtype (uint8 codes for the MX formats)")
     for t in (q_pos, q_first):
-        if t is not None and (t.dtype != torch.int32 or tuple(t.shape) != (n,) or not t.is_cuda
-                              or not t.is_contiguous()):
+        if t is not None and (t.dtype != torch.int32 or tuple(t.shape) != (n,)
+                              or t.device != q.device or not t.is_contiguous()):
             raise ValueError("q_pos / q_first must be contiguous int32 [n] tensors on the GPU")
     if q_start is None:
         q_start = 0 if q_pos is not None else L - n
@@ -222,6 +270,7 @@ def select(q, k, w, topk: int, *, q_scale=None, k_scale=None, q_start=None, para
     import torch
     lib = load_library()
     prob = _problem(q, k, w, topk, q_start, q_pos, q_first, fmt)
+    _scales(prob, q, q_scale, k_scale)
     prm = _params(params)
     need = int(lib.hytopk_select_workspace(ctypes.byref(prob), ctypes.byref(prm) if prm else None))
     if need == 0:
@@ -229,11 +278,12 @@ def select(q, k, w, topk: int, *, q_scale=None, k_scale=None, q_start=None, para
                                  *([None] * 8), 0, None, None))
     if workspace is None:
         workspace = torch.empty(need, dtype=torch.uint8, device=q.device)
+    _workspace(workspace, q.device)
     if out is None:
         idx = torch.empty((prob.n, prob.k), dtype=torch.int32, device=q.device)
         score = torch.empty((prob.n, prob.k), dtype=torch.float32, device=q.device)
     else:
-        idx, score = out
+        idx, score = _outputs(out, prob, q.device)
     st = Stats()
     failed_buf = None
     if with_stats:
@@ -257,8 +307,9 @@ def select_noalloc(q, k, w, topk: int, out, *, q_scale=None, k_scale=None, q_sta
     the device).  Returns ``out`` and, with ``with_stats``, the stats dict."""
     lib = load_library()
     prob = _problem(q, k, w, topk, q_start, q_pos, q_first, fmt)
+    _scales(prob, q, q_scale, k_scale)
     prm = _params(params)
-    idx, score = out
+    idx, score = _outputs(out, prob, q.device)
     st = Stats()
     failed_buf = None
     if with_stats:
@@ -289,10 +340,14 @@ def select_async(q, k, w, topk: int, *, workspace, out, status, q_scale=None, k_
     import torch
     lib = load_library()
     prob = _problem(q, k, w, topk, q_start, q_pos, q_first, fmt)
+    _scales(prob, q, q_scale, k_scale)
     prm = _params(params)
-    idx, score = out
-    if status.dtype != torch.int32 or status.numel() < ASYNC_STATUS_WORDS or not status.is_contiguous():
-        raise ValueError("status must be a contiguous int32 tensor of ASYNC_STATUS_WORDS entries")
+    idx, score = _outputs(out, prob, q.device)
+    _workspace(workspace, q.device)
+    if (status.dtype != torch.int32 or status.numel() < ASYNC_STATUS_WORDS
+            or not status.is_contiguous() or status.device != q.device):
+        raise ValueError("status must be a contiguous int32 tensor of ASYNC_STATUS_WORDS entries "
+                         "on the inputs' device")
     _check(lib.hytopk_select_async(ctypes.byref(prob), ctypes.byref(prm) if prm else None,
                                    _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale), _ptr(w),
                                    _ptr(idx), _ptr(score), _ptr(workspace), workspace.numel(),
@@ -305,10 +360,11 @@ def replay(q, k, w, idx, *, q_scale=None, k_scale=None, q_start=None, out=None, 
     import torch
     lib = load_library()
     prob = _problem(q, k, w, idx.shape[1], q_start, fmt=fmt)
-    if idx.dtype != torch.int32 or not idx.is_contiguous() or idx.shape[0] != prob.n:
-        raise ValueError("idx must be a contiguous int32 [n][k] tensor")
+    _scales(prob, q, q_scale, k_scale)
+    _need(idx, "idx", (prob.n, prob.k), torch.int32, q.device)
     if out is None:
         out = torch.empty(idx.shape, dtype=torch.float32, device=q.device)
+    _need(out, "out", (prob.n, prob.k), torch.float32, q.device)
     _check(lib.hytopk_replay(ctypes.byref(prob), _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale),
                              _ptr(w), _ptr(idx), _ptr(out), _stream(q)))
     return out
@@ -320,14 +376,16 @@ def baseline_select(q, k, w, topk: int, *, q_scale=None, k_scale=None, q_start=N
     import torch
     lib = load_library()
     prob = _problem(q, k, w, topk, q_start, q_pos, q_first, fmt)
+    _scales(prob, q, q_scale, k_scale)
     need = int(lib.hytopk_baseline_workspace(ctypes.byref(prob)))
     if workspace is None:
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    _workspace(workspace, q.device)
     if out is None:
         idx = torch.empty((prob.n, prob.k), dtype=torch.int32, device=q.device)
         score = torch.empty((prob.n, prob.k), dtype=torch.float32, device=q.device)
     else:
-        idx, score = out
+        idx, score = _outputs(out, prob, q.device)
     _check(lib.hytopk_baseline_select(ctypes.byref(prob), _ptr(q), _ptr(q_scale), _ptr(k),
                                       _ptr(k_scale), _ptr(w), _ptr(idx), _ptr(score),
                                       _ptr(workspace), workspace.numel(), _stream(q)))
@@ -349,19 +407,23 @@ def backward(q, k, w, idx, d_score, *, q_scale=None, k_scale=None, q_start=None,
     import torch
     lib = load_library()
     prob = _problem(q, k, w, idx.shape[1], q_start, fmt=fmt)
-    for t, name in ((idx, "idx"), (d_score, "d_score")):
-        if tuple(t.shape) != (prob.n, prob.k) or not t.is_contiguous() or not t.is_cuda:
-            raise ValueError(f"{name} must be a contiguous [n][k] tensor on the GPU")
-    if idx.dtype != torch.int32 or d_score.dtype != torch.float32:
-        raise ValueError("idx must be int32 and d_score float32")
+    _scales(prob, q, q_scale, k_scale)
+    _need(idx, "idx", (prob.n, prob.k), torch.int32, q.device)
+    _need(d_score, "d_score", (prob.n, prob.k), torch.float32, q.device)
     res = dict(out or {})
     shapes = {"dq": (prob.n, prob.H, prob.d), "dw": (prob.n, prob.H), "dk": (prob.L, prob.d)}
+    if set(res) - set(shapes):
+        raise ValueError(f"unknown gradient names in out: {sorted(set(res) - set(shapes))}")
     for name in want:
         if name not in res:
             res[name] = torch.empty(shapes[name], dtype=torch.float32, device=q.device)
+    for name, t in res.items():
+        _need(t, name, shapes[name], torch.float32, q.device)
     if ("dk" in res or prob.dtype != BF16) and workspace is None:
         need = int(lib.hytopk_backward_workspace(ctypes.byref(prob)))
         workspace = torch.empty(max(need, 1), dtype=torch.uint8, device=q.device)
+    if workspace is not None:
+        _workspace(workspace, q.device)
     _check(lib.hytopk_backward(ctypes.byref(prob), _ptr(q), _ptr(q_scale), _ptr(k), _ptr(k_scale),
                                _ptr(w), _ptr(idx), _ptr(d_score), _ptr(res.get("dq")),
                                _ptr(res.get("dw")), _ptr(res.get("dk")), _ptr(workspace),

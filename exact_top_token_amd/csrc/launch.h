@@ -6,7 +6,9 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <atomic>
+#include <mutex>
 
 namespace hk {
 
@@ -14,22 +16,25 @@ namespace hk {
 struct LdsLimit {
   static constexpr int kDevices = 64;
   std::atomic<int> bytes[kDevices];
+  std::mutex mu;  // orders the raises, so the recorded limit is the one in force
 };
 
-// Raises `fn`'s dynamic-LDS limit to `bytes` on the current device, once:
-// later launches that fit the limit make no runtime call (so a launch
+// Raises `fn`'s dynamic-LDS limit to at least `bytes` on the current device,
+// once: later launches that fit the limit make no runtime call (so a launch
 // recorded in a stream capture after a first call outside it makes none).
+// Raises never lower the limit, also when threads race.
 inline hipError_t raise_dynamic_lds(const void* fn, int bytes, LdsLimit& lim) {
   int dev = 0;
   hipError_t e = hipGetDevice(&dev);
   if (e != hipSuccess) return e;
-  const bool cached = dev >= 0 && dev < LdsLimit::kDevices;
-  if (cached && lim.bytes[dev].load(std::memory_order_acquire) >= bytes) return hipSuccess;
-  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
-  if (e != hipSuccess || !cached) return e;
-  int cur = lim.bytes[dev].load(std::memory_order_relaxed);
-  while (cur < bytes && !lim.bytes[dev].compare_exchange_weak(cur, bytes)) {
-  }
+  if (dev < 0 || dev >= LdsLimit::kDevices)
+    return hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, bytes);
+  if (lim.bytes[dev].load(std::memory_order_acquire) >= bytes) return hipSuccess;
+  std::lock_guard<std::mutex> g(lim.mu);
+  const int want = std::max(bytes, lim.bytes[dev].load(std::memory_order_relaxed));
+  e = hipFuncSetAttribute(fn, hipFuncAttributeMaxDynamicSharedMemorySize, want);
+  if (e != hipSuccess) return e;
+  lim.bytes[dev].store(want, std::memory_order_release);
   return hipSuccess;
 }
 

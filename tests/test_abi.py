@@ -93,6 +93,10 @@ def test_null_pointers_and_workspace_errors(lib):
     # fp8 without scales -> -1
     p8 = _prob(dtype=hk.FP8_E4M3)
     assert lib.hytopk_replay(ctypes.byref(p8), fake, None, fake, None, fake, fake, fake, None) == -1
+    pmx4 = _prob(dtype=hk.MXFP4_E2M1)
+    assert lib.hytopk_select(ctypes.byref(pmx4), None, fake, None, fake, fake, fake, fake, None,
+                             fake, 1 << 40, None, None) == -1
+    assert "scale" in lib.hytopk_last_error().decode()
     assert lib.hytopk_status_string(-3).decode() == "bad workspace"
     # misaligned inputs -> -1, before any HIP call: q and k 16-byte aligned,
     # w and the scale arrays 4-byte aligned
@@ -144,3 +148,34 @@ def test_backward_workspace_and_argument_errors(lib):
     bad = _prob(k=4097)
     assert lib.hytopk_backward_workspace(ctypes.byref(bad)) == 0
     assert lib.hytopk_backward(ctypes.byref(bad), *args) == -2
+
+
+def test_binding_rejects_mis_sized_caller_buffers():
+    """The binding checks every caller-given buffer against the problem's
+    sizes before a pointer reaches the library (which cannot see sizes)."""
+    import torch
+    prob = hk.Problem(L=100, n=4, q_start=96, H=2, d=128, k=8, dtype=hk.FP8_E4M3)
+    cpu = torch.device("cpu")
+    good = (torch.empty((4, 8), dtype=torch.int32), torch.empty((4, 8), dtype=torch.float32))
+    hk._outputs(good, prob, cpu)
+    for bad in ((torch.empty((4, 7), dtype=torch.int32), good[1]),
+                (good[0], torch.empty((4, 8), dtype=torch.float64)),
+                (torch.empty((8, 4), dtype=torch.int32).t(), good[1])):
+        with pytest.raises(ValueError):
+            hk._outputs(bad, prob, cpu)
+    q = torch.empty((4, 2, 128), dtype=torch.uint8)
+    hk._scales(prob, q, torch.ones(4), torch.ones(100))
+    with pytest.raises(ValueError):
+        hk._scales(prob, q, torch.ones(4), torch.ones(99))
+    with pytest.raises(ValueError):
+        hk._scales(prob, q, None, torch.ones(100))
+    prob.dtype = hk.MXFP8_E4M3
+    hk._scales(prob, q, torch.ones((4, 2, 4), dtype=torch.uint8), torch.ones((100, 4), dtype=torch.uint8))
+    with pytest.raises(ValueError):
+        hk._scales(prob, q, torch.ones((4, 2, 4)), torch.ones((100, 4), dtype=torch.uint8))
+    prob.dtype = hk.BF16
+    with pytest.raises(ValueError):
+        hk._scales(prob, q, torch.ones(4), None)
+    hk._workspace(torch.empty(64, dtype=torch.uint8), cpu)
+    with pytest.raises(ValueError):
+        hk._workspace(torch.empty(16, dtype=torch.float32), cpu)

@@ -135,3 +135,18 @@ def test_async_graph_replays_match_eager_calls(hk, tiny):
         assert np.array_equal(got[0], _np(ref_idx)), rep
         assert np.array_equal(got[1].view(np.uint32), _np(ref_sc).view(np.uint32)), rep
         assert got[2][0] == 0 and got[2][1] == st["n_failed"], (rep, got[2])
+
+
+def test_binding_rejects_short_outputs_before_any_launch(hk, tiny):
+    d, inp = tiny["dev"], tiny["inp"]
+    ws = torch.empty(hk.select_workspace_bytes(d["q"], d["k"], d["w"], inp.k), dtype=torch.uint8,
+                     device="cuda")
+    status = torch.zeros(hk.ASYNC_STATUS_WORDS, dtype=torch.int32, device="cuda")
+    short = (torch.empty((inp.n - 1, inp.k), dtype=torch.int32, device="cuda"),
+             torch.empty((inp.n - 1, inp.k), dtype=torch.float32, device="cuda"))
+    with pytest.raises(ValueError):
+        hk.select_async(d["q"], d["k"], d["w"], inp.k, workspace=ws, out=short, status=status)
+    with pytest.raises(ValueError):
+        hk.select_noalloc(d["q"], d["k"], d["w"], inp.k, short)
+    with pytest.raises(ValueError):
+        hk.replay(d["q"], d["k"], d["w"], short[0])
