@@ -7,7 +7,9 @@ some cases sequences packed into one key buffer with shuffled query
 positions.  Values are integers, exact in every format, so every selection
 path must return the oracle's indices and scores exactly: the candidate path,
 recovery of a few overflowing queries, the full rescore, the asynchronous
-call, the score-table baseline; replay must return the selected scores."""
+call, the score-table baseline; replay must return the selected scores, and
+the backward at the selected entries (integer upstream gradients) the
+oracle's dq, dw and dk exactly."""
 import numpy as np
 import pytest
 import torch
@@ -118,3 +120,12 @@ def test_sweep_case_every_path_bit_exact(hk, i):
     ok = bits[0] >= 0
     assert np.array_equal(_np(rep).view(np.uint32)[ok], bits[1][ok])
     assert np.all(np.isneginf(_np(rep)[~ok]))
+
+    # the backward at the selected entries, integer upstream gradients: exact
+    g = np.random.default_rng(3000 + i).integers(-3, 4, size=bits[0].shape).astype(np.float32)
+    fk = {x: kw[x] for x in ("q_scale", "k_scale", "fmt") if x in kw}
+    got = hk.backward(q, k, w, idx, torch.from_numpy(g).cuda(), **fk)
+    torch.cuda.synchronize()
+    ref = oracle.backward(inp, bits[0], g)
+    for name in ("dq", "dw", "dk"):
+        assert np.array_equal(_np(got[name]).astype(np.float64), ref[name]), name
