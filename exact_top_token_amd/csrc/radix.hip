@@ -223,6 +223,28 @@ __device__ __forceinline__ void sort_and_emit(uint32_t* sk, uint32_t* sp, uint32
 
 // ----------------------------------------------------------------- candidates
 
+constexpr int kTieRun = 8;  // longest run of equal kept scores ordered in registers
+
+// Ascending order of the len (2 .. kTieRun) distinct positions at p, by
+// odd-even transposition in registers (the padding sorts last).
+__device__ __forceinline__ void sort_short_run(uint32_t* p, int len) {
+  uint32_t v[kTieRun];
+#pragma unroll
+  for (int j = 0; j < kTieRun; ++j) v[j] = j < len ? p[j] : 0xFFFFFFFFu;
+#pragma unroll
+  for (int r = 0; r < kTieRun; ++r) {
+#pragma unroll
+    for (int j = r & 1; j + 1 < kTieRun; j += 2) {
+      const uint32_t a = v[j], b = v[j + 1];
+      v[j] = min(a, b);
+      v[j + 1] = max(a, b);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < kTieRun; ++j)
+    if (j < len) p[j] = v[j];
+}
+
 struct CandShared {
   RadixScratch rs;
   SortScratch ss;
@@ -338,8 +360,10 @@ __global__ void __launch_bounds__(kSelThreads) cand_select_kernel(const int* cnt
   }
   __syncthreads();
   // Order by (score desc, position asc).  Sort on the offset of the key below
-  // the largest kept key (only its significant bits); positions are sorted
-  // first only if two kept entries have equal scores.
+  // the largest kept key (only its significant bits); equal scores then sit
+  // in runs, each ordered by position on its own when it is short; only a
+  // run longer than kTieRun sends the whole row through a position pass and
+  // a stable key pass.
   const uint32_t krange = kmax - v;
   uint32_t* tk = ck;
   uint32_t* tp = ck + topk;
@@ -347,8 +371,8 @@ __global__ void __launch_bounds__(kSelThreads) cand_select_kernel(const int* cnt
   __syncthreads();
   const int kbits = (bit_width(krange) + 3) & ~3;
   const int pbits = (bit_width((uint32_t)(L - 1)) + 3) & ~3;
-  // One sort call site (stage 0: by key; on ties, stage 1: by position,
-  // stage 2: stable by key again), so the sort is inlined once.
+  // One sort call site (stage 0: by key; after a long run of ties, stage 1:
+  // by position, stage 2: stable by key again), so the sort is inlined once.
   uint32_t *rk = sk, *rp = sp, *xk = tk, *xp = tp;
   for (int stage = 0;; ++stage) {
     const bool byp = stage == 1;
@@ -360,10 +384,19 @@ __global__ void __launch_bounds__(kSelThreads) cand_select_kernel(const int* cnt
     }
     if (stage == 2) break;
     if (stage == 0) {
+      // The thread at the start of each run of equal keys orders the run's
+      // positions (runs are disjoint; keys are not written here).
       if (tid == 0) sh.tie = 0;
       __syncthreads();
-      for (int i = tid; i + 1 < need; i += kSelThreads)
-        if (rk[i] == rk[i + 1]) sh.tie = 1;
+      for (int i = tid; i + 1 < need; i += kSelThreads) {
+        if (rk[i] != rk[i + 1] || (i > 0 && rk[i - 1] == rk[i])) continue;  // not a run start
+        int len = 2;
+        while (len <= kTieRun && i + len < need && rk[i + len] == rk[i]) ++len;
+        if (len > kTieRun)
+          sh.tie = 1;
+        else
+          sort_short_run(rp + i, len);
+      }
       __syncthreads();
       if (!sh.tie) break;  // uniform
     }
