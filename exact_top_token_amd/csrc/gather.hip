@@ -8,7 +8,8 @@
 //   M_q = min(M, ctx) evenly spaced keys floor(j * ctx / M_q) of the query's
 //   own context and take the ceil(3k * M_q / ctx)-th best as the threshold.
 //   One query per workgroup; its 64 heads fill four 16-row MFMA blocks, and a
-//   block-wide radix select over the samples (held in LDS) gives tau.
+//   block-wide radix select over the sample scores (in registers for bf16, in
+//   LDS for the scaled formats) gives tau.
 #include "launch.h"
 #include "tile.h"
 
