@@ -445,8 +445,10 @@ __device__ __forceinline__ void sample_scores_direct(const SampleArgs& a, const 
 // sampled keys at or above tau always pass.
 template <int RB4, int D, int FMT, int N>
 // (Three waves per SIMD: the bf16 path fits 168 registers with its 32 sample
-// scores per thread, and its row ring leaves the LDS for three workgroups.)
-__global__ void __launch_bounds__(kSampleThreads) __attribute__((amdgpu_waves_per_eu(3)))
+// scores per thread, and its row ring leaves the LDS for three workgroups;
+// with 64 scores per thread, for sample counts above 8,192, two waves, so
+// that they fit without spilling.)
+__global__ void __launch_bounds__(kSampleThreads) __attribute__((amdgpu_waves_per_eu(N > 32 ? 2 : 3)))
 sample_tau_kernel(SampleArgs a) {
   using T = QueryTile<RB4, D, FMT>;
   extern __shared__ float S[];  // sample scores, M_q entries

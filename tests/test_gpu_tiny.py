@@ -209,3 +209,33 @@ def test_reversed_key_walk_gives_the_same_bits(hk, tiny, shape, monkeypatch):
     assert st0 == st1
     assert np.array_equal(b0[0], b1[0]) and np.array_equal(b0[1].view(np.uint32), b1[1].view(np.uint32))
     assert np.array_equal(b0[0], _np(idx0))
+
+
+@pytest.mark.parametrize("fmt,L,n,H,d,k,M", [
+    ("bf16", 20000, 48, 8, 128, 64, 16384),    # 64 sample scores per thread, one row block
+    ("bf16", 12000, 32, 64, 128, 128, 12000),  # 64 per thread, four row blocks
+    ("mxfp8", 20000, 32, 64, 128, 64, 16384),  # scores in LDS: 64 KB of them
+    ("bf16", 6000, 40, 64, 64, 32, 1000),      # fewer samples than threads x 4
+])
+def test_sample_counts_away_from_the_default(hk, fmt, L, n, H, d, k, M):
+    """m_min = m_max = M sets the sample count: above 8,192 (the register path
+    with 64 scores per thread, the LDS path at its largest) and far below it.
+    Integer scores: thresholds and candidate counts equal the oracle's
+    threshold model with the same M, and the selection equals the oracle."""
+    say(f"sample count {M}: {fmt} L={L} n={n} H={H} d={d} k={k}")
+    inp = datagen.make_custom("mq", L, n, H, d, k, dtype=fmt, dist="int", seed=L + M)
+    dv = to_device(inp)
+    kw = {}
+    if fmt != "bf16":
+        kw = dict(q_scale=dv["q_scale"], k_scale=dv["k_scale"], fmt=fmt)
+    prm = dict(m_min=M, m_max=M)
+    idx, sc, st = hk.select(dv["q"], dv["k"], dv["w"], k, params=prm, with_stats=True, **kw)
+    torch.cuda.synchronize()
+    rows = oracle_rows(inp, range(n))
+    pred = oracle.predict_paths(rows, k, L, cap=6 * k, params=prm)
+    assert st["cand_total"] == sum(p["cnt"] for p in pred["per_query"])
+    assert st["cand_max"] == max(p["cnt"] for p in pred["per_query"])
+    assert st["n_failed"] == pred["n_failed"]
+    ref = [oracle.exact_topk(r, k) for r in rows]
+    assert_exact(inp, range(n), _np(idx), _np(sc), np.stack([r[0] for r in ref]),
+                 np.stack([r[1] for r in ref]))
