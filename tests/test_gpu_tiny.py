@@ -211,24 +211,30 @@ def test_reversed_key_walk_gives_the_same_bits(hk, tiny, shape, monkeypatch):
     assert np.array_equal(b0[0], _np(idx0))
 
 
-@pytest.mark.parametrize("fmt,L,n,H,d,k,M", [
-    ("bf16", 20000, 48, 8, 128, 64, 16384),    # 64 sample scores per thread, one row block
-    ("bf16", 12000, 32, 64, 128, 128, 12000),  # 64 per thread, four row blocks
-    ("mxfp8", 20000, 32, 64, 128, 64, 16384),  # scores in LDS: 64 KB of them
-    ("bf16", 6000, 40, 64, 64, 32, 1000),      # fewer samples than threads x 4
+@pytest.mark.parametrize("fmt,L,n,H,d,k,prm", [
+    # 64 sample scores per thread, one row block
+    ("bf16", 20000, 48, 8, 128, 64, dict(m_min=16384, m_max=16384)),
+    # 64 per thread, four row blocks
+    ("bf16", 12000, 32, 64, 128, 128, dict(m_min=12000, m_max=12000)),
+    # scores in LDS: 64 KB of them
+    ("mxfp8", 20000, 32, 64, 128, 64, dict(m_min=16384, m_max=16384)),
+    # fewer samples than threads x 4, a larger oversampling factor
+    ("bf16", 6000, 40, 64, 64, 32, dict(m_min=1000, m_max=1000, oversample=5)),
+    # M from L / m_div (20000 / 4 = 5000), oversampling by one
+    ("bf16", 20000, 40, 16, 128, 100, dict(m_min=100, m_div=4, oversample=1)),
 ])
-def test_sample_counts_away_from_the_default(hk, fmt, L, n, H, d, k, M):
-    """m_min = m_max = M sets the sample count: above 8,192 (the register path
-    with 64 scores per thread, the LDS path at its largest) and far below it.
-    Integer scores: thresholds and candidate counts equal the oracle's
-    threshold model with the same M, and the selection equals the oracle."""
-    say(f"sample count {M}: {fmt} L={L} n={n} H={H} d={d} k={k}")
-    inp = datagen.make_custom("mq", L, n, H, d, k, dtype=fmt, dist="int", seed=L + M)
+def test_threshold_parameters_away_from_the_default(hk, fmt, L, n, H, d, k, prm):
+    """The sample count M = min(max(m_min, L / m_div), m_max) above 8,192 (the
+    register path with 64 scores per thread, the LDS path at its largest) and
+    far below it, and other oversampling factors.  Integer scores:
+    thresholds and candidate counts equal the oracle's threshold model with
+    the same parameters, and the selection equals the oracle."""
+    say(f"threshold parameters {prm}: {fmt} L={L} n={n} H={H} d={d} k={k}")
+    inp = datagen.make_custom("mq", L, n, H, d, k, dtype=fmt, dist="int", seed=L + n)
     dv = to_device(inp)
     kw = {}
     if fmt != "bf16":
         kw = dict(q_scale=dv["q_scale"], k_scale=dv["k_scale"], fmt=fmt)
-    prm = dict(m_min=M, m_max=M)
     idx, sc, st = hk.select(dv["q"], dv["k"], dv["w"], k, params=prm, with_stats=True, **kw)
     torch.cuda.synchronize()
     rows = oracle_rows(inp, range(n))
