@@ -1,15 +1,15 @@
 """Seeded sweep of small problems against the oracle, bit for bit.
 
 Each case draws its shape from a fixed seed: H from 1 to 64, d from {64, 128}
-(bf16) or 128 (MXFP8 / MXFP4), key counts with ragged tiles, query counts
-with ragged groups, k from 1 up to 2,048 (also above the context), and for
-some cases sequences packed into one key buffer with shuffled query
-positions.  Values are integers, exact in every format, so every selection
-path must return the oracle's indices and scores exactly: the candidate path,
-recovery of a few overflowing queries, the full rescore, the asynchronous
-call, the score-table baseline; replay must return the selected scores, and
-the backward at the selected entries (integer upstream gradients) the
-oracle's dq, dw and dk exactly."""
+(bf16) or 128 (per-token FP8 with power-of-two scales, MXFP8, MXFP4), key
+counts with ragged tiles, query counts with ragged groups, k from 1 up to
+2,048 (also above the context), and for some cases sequences packed into one
+key buffer with shuffled query positions.  Values are integers, exact in
+every format, so every selection path must return the oracle's indices and
+scores exactly: the candidate path, recovery of a few overflowing queries,
+the full rescore, the asynchronous call, the score-table baseline; replay
+must return the selected scores, and the backward at the selected entries
+(integer upstream gradients) the oracle's dq, dw and dk exactly."""
 import numpy as np
 import pytest
 import torch
@@ -20,14 +20,28 @@ from gpu_util import assert_exact, say, to_device
 
 pytestmark = pytest.mark.gpu
 
-N_CASES = 14
+N_CASES = 18
+
+
+def _as_fp8(base, rng):
+    """The same integer values as OCP E4M3 codes with per-token scales drawn
+    from 2^-1, 2^0, 2^1 (every product and sum stays exact)."""
+    qv = (base.q.astype(np.uint32) << 16).view(np.float32)
+    kv = (base.k_.astype(np.uint32) << 16).view(np.float32)
+    qs = np.exp2(rng.integers(-1, 2, size=base.n)).astype(np.float32)
+    ks = np.exp2(rng.integers(-1, 2, size=base.L)).astype(np.float32)
+    inp = datagen.Inputs("sweep", base.L, base.n, base.H, base.d, base.k, "fp8",
+                         datagen.f32_to_e4m3(qv), datagen.f32_to_e4m3(kv), base.w, qs, ks)
+    inp.q_pos, inp.q_first = base.q_pos, base.q_first
+    return inp
 
 
 def _case(i):
     rng = np.random.default_rng(1000 + i)
-    fmt = ["bf16", "bf16", "bf16", "mxfp8", "mxfp4"][i % 5]
+    fmt = "fp8" if i >= 14 else ["bf16", "bf16", "bf16", "mxfp8", "mxfp4"][i % 5]
     H = int(rng.integers(1, 65))
     d = int(rng.choice([64, 128])) if fmt == "bf16" else 128
+    draw = "bf16" if fmt == "fp8" else fmt  # FP8 codes are made from the bf16 draw below
     packed = i % 3 == 2
     if packed:
         lens = [int(x) for x in rng.integers(40, 1500, size=int(rng.integers(2, 5)))]
@@ -45,11 +59,11 @@ def _case(i):
          k_hi][kind]
     seed = 2000 + i
     if packed:
-        inp = datagen.make_packed("sweep", lens, chunks, H=H, d=d, k=k, dtype=fmt, dist="int",
+        inp = datagen.make_packed("sweep", lens, chunks, H=H, d=d, k=k, dtype=draw, dist="int",
                                   seed=seed)
     else:
-        inp = datagen.make_custom("sweep", L, n, H, d, k, dtype=fmt, dist="int", seed=seed)
-    return inp
+        inp = datagen.make_custom("sweep", L, n, H, d, k, dtype=draw, dist="int", seed=seed)
+    return _as_fp8(inp, rng) if fmt == "fp8" else inp
 
 
 @pytest.fixture(scope="module")
